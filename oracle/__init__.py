@@ -1,0 +1,15 @@
+"""Float64 CPU oracle for shared-QK LSH self-attention (test infrastructure only).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package; the library itself never does.
+"""
+from .lsh_oracle import (  # noqa: F401
+    attend_positions,
+    chunk_attention_round,
+    combine_rounds,
+    exact_projection_margin,
+    lsh_attention,
+    lsh_attention_head,
+    lsh_hash,
+    lsh_sort,
+)

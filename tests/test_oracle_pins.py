@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test ties one part of the oracle to something other than itself: hand-worked
+examples (``tests/golden/hand_examples.json``), exact rational arithmetic, closed
+forms, invariants, a library routine for the special case that is plain
+attention, or a pure-Python brute force on tiny inputs.  A plausible slip in the
+oracle (dropped self mask, wrong window, flipped sign convention, wrong tie-break,
+missing round weights, causal off by one) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from efficient_long_sequence_lsh_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- hash ----
+
+@pytest.mark.parametrize("case", _golden()["hash"]["cases"], ids=lambda c: c["note"][:40])
+def test_hash_hand_examples(case):
+    x = np.asarray([case["x"]], np.float64)
+    R = np.asarray(case["R"], np.float64)[None]
+    b, m = oracle.lsh_hash(x, R, case["n_buckets"])
+    assert int(b[0, 0]) == case["bucket"]
+    assert m[0, 0] == pytest.approx(case["margin"], abs=1e-12)
+
+
+def test_hash_single_bucket_is_zero():
+    x = np.random.default_rng(0).standard_normal((7, 3))
+    b, m = oracle.lsh_hash(x, np.zeros((2, 3, 0)), 1)
+    assert b.shape == (2, 7) and not b.any() and np.isinf(m).all()
+
+
+def test_hash_odd_bucket_count_rejected():
+    with pytest.raises(ValueError):
+        oracle.lsh_hash(np.zeros((2, 2)), np.zeros((1, 2, 1)), 3)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hash_matches_exact_rational_brute_force(seed):
+    """P-1: projections evaluated exactly with fractions on tiny inputs."""
+    g = np.random.default_rng(100 + seed)
+    L, d = int(g.integers(1, 12)), int(g.integers(1, 8))
+    n_buckets = int(2 * g.integers(1, 5))
+    r = int(g.integers(1, 3))
+    x = g.standard_normal((L, d))
+    R = g.standard_normal((r, d, n_buckets // 2))
+    b, m = oracle.lsh_hash(x, R, n_buckets)
+    for rho in range(r):
+        for i in range(L):
+            best, gap = oracle.exact_projection_margin(x[i], R[rho], n_buckets)
+            assert b[rho, i] == best
+            assert m[rho, i] == pytest.approx(float(gap), rel=1e-9, abs=1e-12)
+
+
+def test_hash_identity_rotation_closed_form():
+    """With R = I the bucket is the largest-magnitude coordinate (+b/2 if negative)."""
+    g = np.random.default_rng(7)
+    d = 8
+    x = g.standard_normal((200, d))
+    b, _ = oracle.lsh_hash(x, np.eye(d)[None], 2 * d)
+    k = np.argmax(np.abs(x), axis=1)
+    expect = np.where(x[np.arange(200), k] >= 0, k, k + d)
+    assert np.array_equal(b[0], expect)
+
+
+def test_hash_scale_and_negation_invariants():
+    g = np.random.default_rng(11)
+    x = g.standard_normal((300, 16))
+    R = g.standard_normal((2, 16, 12))
+    b, m = oracle.lsh_hash(x, R, 24)
+    b2, _ = oracle.lsh_hash(3.5 * x, R, 24)
+    assert np.array_equal(b, b2)                        # h(a x) = h(x), a > 0
+    bn, _ = oracle.lsh_hash(-x, R, 24)
+    ok = m > 0
+    assert np.array_equal(bn[ok], ((b + 12) % 24)[ok])  # h(-x) = h(x) + b/2 mod b
+
+
+# ---------------------------------------------------------------- sort ----
+
+def test_sort_matches_python_sorted_and_is_stable():
+    g = np.random.default_rng(3)
+    buckets = g.integers(0, 6, size=(3, 50))
+    perm, inv = oracle.lsh_sort(buckets)
+    for rho in range(3):
+        expect = sorted(range(50), key=lambda i: (buckets[rho, i], i))
+        assert list(perm[rho]) == expect
+        assert np.array_equal(inv[rho][perm[rho]], np.arange(50))
+        keys = buckets[rho, perm[rho]]
+        assert np.all(np.diff(keys) >= 0)
+        same = np.diff(keys) == 0
+        assert np.all(np.diff(perm[rho])[same] > 0)
+
+
+# ------------------------------------------------------ brute force -------
+
+def _brute_force_forward(x, v, R, n_buckets, chunk_len, causal):
+    """Pure-Python loops over the definition: hash, sort, windows, masks, combine."""
+    L, d = len(x), len(x[0])
+    r = R.shape[0] if n_buckets > 1 else 1
+    m = min(chunk_len, L)
+    per_round = []
+    for rho in range(r):
+        if n_buckets == 1:
+            bucket = [0] * L
+        else:
+            bucket = []
+            for i in range(L):
+                y = []
+                for k in range(n_buckets // 2):
+                    y.append(math.fsum(x[i][j] * R[rho][j][k] for j in range(d)))
+                y = y + [-t for t in y]
+                best = 0
+                for k in range(len(y)):
+                    if y[k] > y[best]:
+                        best = k
+                bucket.append(best)
+        order = sorted(range(L), key=lambda i: (bucket[i], i))
+        slot = {p: s for s, p in enumerate(order)}
+        res = {}
+        for i in range(L):
+            c = slot[i] // m
+            window = [order[s] for s in range(max(0, (c - 1) * m), (c + 1) * m)]
+            targets = [j for j in window if j != i and (not causal or j < i)]
+            if not targets:
+                res[i] = None
+                continue
+            scores = [math.fsum(x[i][t] * x[j][t] for t in range(d)) / math.sqrt(d) for j in targets]
+            top = max(scores)
+            w = [math.exp(s - top) for s in scores]
+            tot = math.fsum(w)
+            o = [math.fsum(w[k] * v[targets[k]][t] for k in range(len(targets))) / tot for t in range(len(v[0]))]
+            res[i] = (top + math.log(tot), o)
+        per_round.append(res)
+    out = []
+    for i in range(L):
+        got = [pr[i] for pr in per_round if pr[i] is not None]
+        if not got:
+            out.append(list(v[i]))
+            continue
+        top = max(z for z, _ in got)
+        w = [math.exp(z - top) for z, _ in got]
+        tot = math.fsum(w)
+        out.append([math.fsum(w[k] * got[k][1][t] for k in range(len(got))) / tot for t in range(len(v[0]))])
+    return np.asarray(out)
+
+
+@pytest.mark.parametrize("chunk_len", [1, 2, 4, 32])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_rounds", [1, 3])
+def test_forward_matches_pure_python_brute_force(chunk_len, causal, n_rounds):
+    """P-6: whole pipeline, tiny L, explicit loops."""
+    g = np.random.default_rng(1000 + 10 * chunk_len + 2 * causal + n_rounds)
+    L, d, nb = 16, 4, 4
+    x = g.standard_normal((L, d))
+    v = g.standard_normal((L, 3))
+    R = g.standard_normal((n_rounds, d, nb // 2))
+    got = oracle.lsh_attention_head(x, v, R, nb, chunk_len, causal)["out"]
+    want = _brute_force_forward(x.tolist(), v.tolist(), R, nb, chunk_len, causal)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------- hand-worked attention ----
+
+@pytest.mark.parametrize("case", _golden()["attention"]["cases"], ids=lambda c: c["note"][:40])
+def test_attention_hand_examples(case):
+    x = np.asarray(case["x"], np.float64)
+    v = np.asarray(case["v"], np.float64)
+    res = oracle.lsh_attention_head(x, v, None, case["n_buckets"], case["chunk_len"], case["causal"])
+    rows = case.get("check_rows", list(range(len(x))))
+    np.testing.assert_allclose(res["out"][rows], np.asarray(case["out"]), rtol=0, atol=1e-12)
+
+
+# -------------------------------------------- special case = attention ----
+
+def _dense_masked_attention_torch(x, v, causal):
+    """Full shared-QK attention with the diagonal masked, via torch's SDPA (float64 CPU)."""
+    import torch
+
+    L = x.shape[0]
+    xt = torch.from_numpy(x)[None, None]
+    vt = torch.from_numpy(v)[None, None]
+    allowed = ~torch.eye(L, dtype=torch.bool)
+    if causal:
+        allowed &= torch.ones(L, L, dtype=torch.bool).tril()
+    out = torch.nn.functional.scaled_dot_product_attention(xt, xt, vt, attn_mask=allowed)
+    return out[0, 0].numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_bucket_one_chunk_is_full_attention(causal):
+    """P-4: with one bucket and chunk_len >= L the method is plain self-masked attention."""
+    inp = workloads.make_inputs("tiny_1k_full")
+    x = inp.qk[0, 0].astype(np.float64)
+    v = inp.v[0, 0].astype(np.float64)
+    res = oracle.lsh_attention_head(x, v, None, 1, 1024, causal)
+    want = _dense_masked_attention_torch(x, v, causal)
+    lo = 1 if causal else 0
+    np.testing.assert_allclose(res["out"][lo:], want[lo:], rtol=0, atol=1e-10)
+    if causal:
+        np.testing.assert_array_equal(res["out"][0], v[0])   # nothing earlier: falls back to itself
+
+
+def test_chunk_covering_sequence_ignores_buckets():
+    """P-5: chunk_len >= L with many buckets and rounds is still full attention."""
+    g = np.random.default_rng(5)
+    L, d = 96, 8
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((3, d, 8))
+    res = oracle.lsh_attention_head(x, v, R, 16, 128, False)
+    np.testing.assert_allclose(res["out"], _dense_masked_attention_torch(x, v, False), atol=1e-11, rtol=0)
+
+
+# -------------------------------------------------------- invariances -----
+
+def test_shuffling_slots_inside_chunks_keeps_output():
+    """P-7a: chunk membership, not order inside a chunk, defines the windows."""
+    g = np.random.default_rng(21)
+    L, d, m = 256, 16, 16
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((2, d, 8))
+    base = oracle.lsh_attention_head(x, v, R, 16, m, True)
+    perm = base["perm"].copy()
+    for rho in range(2):
+        for c in range(L // m):
+            seg = perm[rho, c * m:(c + 1) * m]
+            perm[rho, c * m:(c + 1) * m] = g.permutation(seg)
+    shuffled = oracle.lsh_attention_head(x, v, R, 16, m, True, perm=perm)
+    np.testing.assert_allclose(shuffled["out"], base["out"], atol=1e-12, rtol=0)
+
+
+def test_within_bucket_order_invariance_for_bucket_aligned_input():
+    """P-7b: every bucket holds exactly m positions, so reordering inside a bucket keeps chunks."""
+    g = np.random.default_rng(22)
+    L, d, nb, m = 1024, 64, 32, 32
+    R = g.standard_normal((1, d, nb // 2))
+    dirs = np.concatenate([R[0].T, -R[0].T])                 # bucket k <-> direction of y_k
+    dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
+    owner = g.permutation(np.repeat(np.arange(nb), L // nb))
+    x = 3.0 * dirs[owner] + 0.05 * g.standard_normal((L, d))
+    v = g.standard_normal((L, d))
+    base = oracle.lsh_attention_head(x, v, R, nb, m, False)
+    assert np.array_equal(np.bincount(base["buckets"][0], minlength=nb), np.full(nb, m))
+    perm = base["perm"].copy()
+    for k in range(nb):
+        perm[0, k * m:(k + 1) * m] = perm[0, k * m:(k + 1) * m][::-1]
+    rev = oracle.lsh_attention_head(x, v, R, nb, m, False, perm=perm)
+    np.testing.assert_allclose(rev["out"], base["out"], atol=1e-12, rtol=0)
+
+
+def test_combine_equals_one_softmax_over_multiset_of_keys():
+    """P-8i: logsumexp-weighted rounds = one softmax over the keys of all rounds, with repeats."""
+    g = np.random.default_rng(31)
+    L, d, m = 64, 8, 8
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((3, d, 4))
+    res = oracle.lsh_attention_head(x, v, R, 8, m, False)
+    for i in range(L):
+        keys = []
+        for rho in range(3):
+            c = res["inv"][rho, i] // m
+            win = res["perm"][rho, max(0, (c - 1) * m):(c + 1) * m]
+            keys.extend(int(j) for j in win if j != i)
+        s = np.array([x[i] @ x[j] for j in keys]) / math.sqrt(d)
+        w = np.exp(s - s.max())
+        want = (w / w.sum()) @ v[keys]
+        np.testing.assert_allclose(res["out"][i], want, atol=1e-12, rtol=0)
+
+
+def test_identical_rounds_equal_one_round():
+    """P-8ii: repeating the same rotation r times gives the single-round result."""
+    g = np.random.default_rng(32)
+    L, d = 128, 8
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R1 = g.standard_normal((1, d, 8))
+    one = oracle.lsh_attention_head(x, v, R1, 16, 16, True)["out"]
+    three = oracle.lsh_attention_head(x, v, np.repeat(R1, 3, axis=0), 16, 16, True)["out"]
+    np.testing.assert_allclose(three, one, atol=1e-12, rtol=0)
+
+
+def test_causal_output_ignores_later_values():
+    """P-9: under the causal mask out_i does not depend on v_j for j > i."""
+    g = np.random.default_rng(41)
+    L, d = 256, 8
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((2, d, 8))
+    base = oracle.lsh_attention_head(x, v, R, 16, 16, True)["out"]
+    cut = 100
+    v2 = v.copy()
+    v2[cut + 1:] = g.standard_normal((L - cut - 1, d)) * 10
+    got = oracle.lsh_attention_head(x, v2, R, 16, 16, True)["out"]
+    np.testing.assert_array_equal(got[:cut + 1], base[:cut + 1])
+    assert not np.allclose(got[cut + 1:], base[cut + 1:])
+
+
+def test_linear_in_values():
+    """P-10: the hash and the weights depend on qk only, so the output is linear in v."""
+    g = np.random.default_rng(42)
+    L, d = 128, 8
+    x = g.standard_normal((L, d))
+    v1, v2 = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((2, d, 4))
+    f = lambda vv: oracle.lsh_attention_head(x, vv, R, 8, 8, False)["out"]
+    np.testing.assert_allclose(f(2.5 * v1 + v2), 2.5 * f(v1) + f(v2), atol=1e-12, rtol=0)
+
+
+def test_chunk_of_one_attends_to_previous_slot_only():
+    """P-11: m = 1, one round: slot s sees only slot s-1; slot 0 falls back to itself."""
+    g = np.random.default_rng(51)
+    L, d = 64, 8
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((1, d, 4))
+    res = oracle.lsh_attention_head(x, v, R, 8, 1, False)
+    perm = res["perm"][0]
+    np.testing.assert_array_equal(res["out"][perm[0]], v[perm[0]])
+    for s in range(1, L):
+        np.testing.assert_allclose(res["out"][perm[s]], v[perm[s - 1]], atol=1e-15, rtol=0)
+
+
+def test_zero_queries_give_window_means():
+    """x = 0: one bucket, identity order, uniform weights: out_i is the mean of its window."""
+    g = np.random.default_rng(52)
+    L, m = 48, 8
+    x = np.zeros((L, 4))
+    v = g.standard_normal((L, 2))
+    for causal in (False, True):
+        out = oracle.lsh_attention_head(x, v, None, 1, m, causal)["out"]
+        for i in range(L):
+            c = i // m
+            keys = [j for j in range(max(0, (c - 1) * m), (c + 1) * m) if j != i and (not causal or j < i)]
+            want = v[keys].mean(axis=0) if keys else v[i]
+            np.testing.assert_allclose(out[i], want, atol=1e-14, rtol=0)
+
+
+def test_per_position_form_matches_chunked_form():
+    g = np.random.default_rng(61)
+    L, d = 256, 16
+    x, v = g.standard_normal((L, d)), g.standard_normal((L, d))
+    R = g.standard_normal((4, d, 16))
+    res = oracle.lsh_attention_head(x, v, R, 32, 16, True)
+    pos = np.arange(L)
+    out, o, z = oracle.attend_positions(x, v, res["perm"], res["inv"], pos, 16, True)
+    np.testing.assert_allclose(out, res["out"], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(o, res["o"], atol=1e-12, rtol=0)
+    np.testing.assert_array_equal(np.isinf(z), np.isinf(res["z"]))
+
+
+def test_ragged_chunking_rejected():
+    with pytest.raises(ValueError):
+        oracle.chunk_attention_round(np.zeros((10, 2)), np.zeros((10, 2)), np.arange(10), 4, False)
+
+
+def test_memory_figure_of_dense_attention():
+    """P-12: the dense 64K x 64K float32 matrix is 16 GiB (about 16 GB)."""
+    mem = _golden()["memory"]
+    n = workloads.dense_score_matrix_bytes(mem["seq_len"], mem["batch"], 1, mem["bytes_per_value"])
+    assert n == 16 * 2 ** 30
+    assert round(n / 2 ** 30) == mem["approx_gb"]
