@@ -1,0 +1,299 @@
+// C ABI of the LSH attention library: argument validation (pure host code,
+// run before any HIP call), workspace carving and the launch sequence.
+#include "../../include/reformer_lsh.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <limits>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace {
+
+constexpr int kMaxBuckets = 16384;
+constexpr int kMaxSegments = 65535;   // grid y-dimension bound for per-segment launches
+
+thread_local char g_last_error[512] = "";
+
+rlsh_status_t fail(rlsh_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+rlsh_status_t ok() {
+  g_last_error[0] = '\0';
+  return RLSH_OK;
+}
+
+rlsh_status_t hip_status(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(RLSH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+  return ok();
+}
+
+// Shape checks shared by all entry points.  n_buckets < 0 means "not used".
+rlsh_status_t check_shape(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets, int chunk_len) {
+  if (batch < 1 || heads < 1 || seq_len < 1 || n_rounds < 1)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "batch, heads, seq_len and n_rounds must be >= 1 (got %d, %d, %d, %d)",
+                batch, heads, seq_len, n_rounds);
+  const long long total = static_cast<long long>(batch) * heads * n_rounds * seq_len;
+  if (total >= (1LL << 31))
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "batch*heads*n_rounds*seq_len = %lld must be < 2^31", total);
+  if (static_cast<long long>(batch) * heads * n_rounds > kMaxSegments)
+    return fail(RLSH_ERR_UNSUPPORTED, "batch*heads*n_rounds must be <= %d", kMaxSegments);
+  if (d_head >= 0 && d_head != 64 && d_head != 128)
+    return fail(RLSH_ERR_UNSUPPORTED, "d_head must be 64 or 128 (got %d)", d_head);
+  if (n_buckets >= 0) {
+    if (n_buckets < 1 || (n_buckets != 1 && (n_buckets % 2) != 0))
+      return fail(RLSH_ERR_INVALID_ARGUMENT, "n_buckets must be 1 or even (got %d)", n_buckets);
+    if (n_buckets > kMaxBuckets)
+      return fail(RLSH_ERR_UNSUPPORTED, "n_buckets must be <= %d (got %d)", kMaxBuckets, n_buckets);
+  }
+  if (chunk_len >= 0) {
+    if (chunk_len < 1) return fail(RLSH_ERR_INVALID_ARGUMENT, "chunk_len must be >= 1 (got %d)", chunk_len);
+    const int m = std::min(chunk_len, seq_len);
+    if (seq_len % m != 0)
+      return fail(RLSH_ERR_INVALID_ARGUMENT, "seq_len %d must be a multiple of chunk_len %d (or chunk_len >= seq_len)",
+                  seq_len, chunk_len);
+  }
+  return ok();
+}
+
+// Rows are moved with 16-byte vector loads and stores.
+rlsh_status_t check_aligned(const void* p, const char* name) {
+  if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0u)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return ok();
+}
+
+rlsh_status_t check_dtype(rlsh_dtype_t dtype) {
+  if (dtype != RLSH_F32 && dtype != RLSH_BF16) return fail(RLSH_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  return ok();
+}
+
+size_t tokens(int batch, int heads, int seq_len) {
+  return static_cast<size_t>(batch) * heads * seq_len;
+}
+
+size_t a256(size_t x) { return rlsh::align_up(x, 256); }
+
+size_t hash_ws(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets) {
+  if (n_buckets <= 1) return 0;
+  return rlsh::hash_scratch(rlsh::make_hash_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets)).total;
+}
+
+size_t sort_ws(int batch, int heads, int seq_len, int n_rounds, int n_buckets) {
+  return rlsh::sort_scratch_bytes(rlsh::make_sort_shape(batch * heads * n_rounds, seq_len, n_buckets));
+}
+
+size_t attend_ws(int batch, int heads, int seq_len, int d_head, int n_rounds) {
+  const size_t n = tokens(batch, heads, seq_len) * n_rounds;
+  return a256(n * d_head * sizeof(float)) + a256(n * sizeof(float));
+}
+
+// Full pipeline layout: buckets | perm | region (o_rounds, aliased earlier by
+// the hash and sort scratch, which are dead once attention starts) | z_rounds.
+struct FullLayout {
+  size_t buckets, perm, region, z, total;
+};
+
+FullLayout full_layout(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets) {
+  const size_t n = tokens(batch, heads, seq_len) * n_rounds;
+  FullLayout f{};
+  f.buckets = 0;
+  f.perm = a256(n * sizeof(int32_t));
+  size_t region = a256(n * d_head * sizeof(float));
+  region = std::max(region, a256(hash_ws(batch, heads, seq_len, d_head, n_rounds, n_buckets)));
+  region = std::max(region, a256(sort_ws(batch, heads, seq_len, n_rounds, n_buckets)));
+  f.region = f.perm + a256(n * sizeof(int32_t));
+  f.z = f.region + region;
+  f.total = f.z + a256(n * sizeof(float));
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* reformer_lsh_status_string(rlsh_status_t status) {
+  switch (status) {
+    case RLSH_OK: return "RLSH_OK";
+    case RLSH_ERR_INVALID_ARGUMENT: return "RLSH_ERR_INVALID_ARGUMENT";
+    case RLSH_ERR_UNSUPPORTED: return "RLSH_ERR_UNSUPPORTED";
+    case RLSH_ERR_WORKSPACE_TOO_SMALL: return "RLSH_ERR_WORKSPACE_TOO_SMALL";
+    case RLSH_ERR_HIP: return "RLSH_ERR_HIP";
+  }
+  return "RLSH_UNKNOWN_STATUS";
+}
+
+const char* reformer_lsh_last_error(void) { return g_last_error; }
+
+int reformer_lsh_version(void) { return 10000; }
+
+size_t reformer_lsh_hash_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets) {
+  if (check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, -1) != RLSH_OK) return 0;
+  return hash_ws(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+}
+
+rlsh_status_t reformer_lsh_hash(const void* qk, rlsh_dtype_t dtype, const float* rotations, int batch, int heads,
+                                int seq_len, int d_head, int n_rounds, int n_buckets, int32_t* buckets,
+                                int32_t* n_near_ties, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, -1);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (qk == nullptr || buckets == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "qk and buckets must be non-null");
+  if ((st = check_aligned(qk, "qk")) != RLSH_OK) return st;
+  if ((st = check_aligned(workspace, "workspace")) != RLSH_OK) return st;
+  const size_t need = hash_ws(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+  if (n_buckets > 1) {
+    if (rotations == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "rotations must be non-null when n_buckets > 1");
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "hash workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  }
+  const size_t n = tokens(batch, heads, seq_len) * n_rounds;
+  if (n_buckets == 1) {
+    hipError_t e = rlsh::launch_fill_zero_buckets(buckets, n, stream);
+    if (e == hipSuccess && n_near_ties != nullptr) e = rlsh::launch_fill_zero_buckets(n_near_ties, 1, stream);
+    return hip_status(e, "reformer_lsh_hash");
+  }
+  const rlsh::HashShape hs = rlsh::make_hash_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+  return hip_status(rlsh::launch_hash(qk, dtype == RLSH_BF16, rotations, hs, buckets, n_near_ties, workspace, stream),
+                    "reformer_lsh_hash");
+}
+
+size_t reformer_lsh_sort_workspace_bytes(int batch, int heads, int seq_len, int n_rounds, int n_buckets) {
+  if (check_shape(batch, heads, seq_len, -1, n_rounds, n_buckets, -1) != RLSH_OK) return 0;
+  return sort_ws(batch, heads, seq_len, n_rounds, n_buckets);
+}
+
+rlsh_status_t reformer_lsh_sort(const int32_t* buckets, int batch, int heads, int seq_len, int n_rounds,
+                                int n_buckets, int32_t* perm, int32_t* inv_perm, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, -1, n_rounds, n_buckets, -1);
+  if (st != RLSH_OK) return st;
+  if (buckets == nullptr || perm == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "buckets and perm must be non-null");
+  if ((st = check_aligned(workspace, "workspace")) != RLSH_OK) return st;
+  const size_t need = sort_ws(batch, heads, seq_len, n_rounds, n_buckets);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "sort workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  const rlsh::SortShape ss = rlsh::make_sort_shape(batch * heads * n_rounds, seq_len, n_buckets);
+  return hip_status(rlsh::launch_sort(buckets, ss, perm, inv_perm, workspace, stream), "reformer_lsh_sort");
+}
+
+rlsh_status_t reformer_lsh_chunk_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm,
+                                        int batch, int heads, int seq_len, int d_head, int n_rounds, int chunk_len,
+                                        int causal, float* o_rounds, float* z_rounds, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (qk == nullptr || v == nullptr || perm == nullptr || o_rounds == nullptr || z_rounds == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "qk, v, perm, o_rounds and z_rounds must be non-null");
+  if ((st = check_aligned(qk, "qk")) != RLSH_OK || (st = check_aligned(v, "v")) != RLSH_OK ||
+      (st = check_aligned(o_rounds, "o_rounds")) != RLSH_OK)
+    return st;
+  return hip_status(rlsh::launch_chunk_attend(qk, v, dtype == RLSH_BF16, perm, batch * heads, seq_len, d_head, n_rounds,
+                                              chunk_len, causal != 0, o_rounds, z_rounds, stream),
+                    "reformer_lsh_chunk_attend");
+}
+
+rlsh_status_t reformer_lsh_combine(const float* o_rounds, const float* z_rounds, const void* v, rlsh_dtype_t dtype,
+                                   int batch, int heads, int seq_len, int d_head, int n_rounds, void* out,
+                                   hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, -1, -1);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (o_rounds == nullptr || z_rounds == nullptr || v == nullptr || out == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "o_rounds, z_rounds, v and out must be non-null");
+  if ((st = check_aligned(o_rounds, "o_rounds")) != RLSH_OK || (st = check_aligned(v, "v")) != RLSH_OK ||
+      (st = check_aligned(out, "out")) != RLSH_OK)
+    return st;
+  return hip_status(rlsh::launch_combine(o_rounds, z_rounds, v, dtype == RLSH_BF16, batch * heads, seq_len, d_head,
+                                         n_rounds, out, stream),
+                    "reformer_lsh_combine");
+}
+
+size_t reformer_lsh_attend_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds) {
+  if (check_shape(batch, heads, seq_len, d_head, n_rounds, -1, -1) != RLSH_OK) return 0;
+  return attend_ws(batch, heads, seq_len, d_head, n_rounds);
+}
+
+rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int batch,
+                                  int heads, int seq_len, int d_head, int n_rounds, int chunk_len, int causal,
+                                  void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (qk == nullptr || v == nullptr || perm == nullptr || out == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "qk, v, perm and out must be non-null");
+  if ((st = check_aligned(qk, "qk")) != RLSH_OK || (st = check_aligned(v, "v")) != RLSH_OK ||
+      (st = check_aligned(out, "out")) != RLSH_OK || (st = check_aligned(workspace, "workspace")) != RLSH_OK)
+    return st;
+  const size_t need = attend_ws(batch, heads, seq_len, d_head, n_rounds);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "attend workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  const size_t n = tokens(batch, heads, seq_len) * n_rounds;
+  float* o = static_cast<float*>(workspace);
+  float* z = reinterpret_cast<float*>(static_cast<char*>(workspace) + a256(n * d_head * sizeof(float)));
+  const bool bf16 = dtype == RLSH_BF16;
+  hipError_t e = rlsh::launch_chunk_attend(qk, v, bf16, perm, batch * heads, seq_len, d_head, n_rounds, chunk_len,
+                                           causal != 0, o, z, stream);
+  if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, batch * heads, seq_len, d_head, n_rounds, out, stream);
+  return hip_status(e, "reformer_lsh_attend");
+}
+
+size_t reformer_lsh_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                                    int chunk_len) {
+  if (check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len) != RLSH_OK) return 0;
+  return full_layout(batch, heads, seq_len, d_head, n_rounds, n_buckets).total;
+}
+
+rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float* rotations, rlsh_dtype_t dtype,
+                                     int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                                     int chunk_len, int causal, void* out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (qk == nullptr || v == nullptr || out == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "qk, v and out must be non-null");
+  if ((st = check_aligned(qk, "qk")) != RLSH_OK || (st = check_aligned(v, "v")) != RLSH_OK ||
+      (st = check_aligned(out, "out")) != RLSH_OK || (st = check_aligned(workspace, "workspace")) != RLSH_OK)
+    return st;
+  if (n_buckets > 1 && rotations == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "rotations must be non-null when n_buckets > 1");
+  const FullLayout f = full_layout(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+  if (workspace == nullptr || workspace_bytes < f.total)
+    return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", f.total, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* bk = reinterpret_cast<int32_t*>(ws + f.buckets);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + f.perm);
+  void* region = ws + f.region;
+  float* o = reinterpret_cast<float*>(region);
+  float* z = reinterpret_cast<float*>(ws + f.z);
+  const bool bf16 = dtype == RLSH_BF16;
+  const int bh = batch * heads;
+  hipError_t e = hipSuccess;
+  if (n_buckets > 1) {
+    const rlsh::HashShape hs = rlsh::make_hash_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+    e = rlsh::launch_hash(qk, bf16, rotations, hs, bk, nullptr, region, stream);
+    if (e == hipSuccess) {
+      const rlsh::SortShape ss = rlsh::make_sort_shape(bh * n_rounds, seq_len, n_buckets);
+      e = rlsh::launch_sort(bk, ss, perm, nullptr, region, stream);
+    }
+  } else {
+    // One bucket: every round keeps the original order.
+    const rlsh::SortShape ss = rlsh::make_sort_shape(bh * n_rounds, seq_len, 1);
+    e = rlsh::launch_sort(nullptr, ss, perm, nullptr, nullptr, stream);
+  }
+  if (e == hipSuccess)
+    e = rlsh::launch_chunk_attend(qk, v, bf16, perm, bh, seq_len, d_head, n_rounds, chunk_len, causal != 0, o, z, stream);
+  if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, bh, seq_len, d_head, n_rounds, out, stream);
+  return hip_status(e, "reformer_lsh_attention");
+}
+
+}  // extern "C"

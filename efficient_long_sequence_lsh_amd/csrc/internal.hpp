@@ -1,0 +1,58 @@
+// Launchers shared between the kernel sources and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rlsh {
+
+// Geometry of the hash stage (all derived on the host from the ABI arguments).
+struct HashShape {
+  int n_tokens;    // batch * heads * seq_len
+  int seq_len;
+  int d;           // 64 or 128
+  int n_rounds;
+  int n_buckets;   // even, >= 2
+  int half;        // n_buckets / 2
+  int n_ctiles;    // ceil(half / 32): column tiles of 32 rotation columns
+  int code_bits;   // bits of the candidate code packed into a projection key
+};
+
+HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds, int n_buckets);
+
+// Byte sizes of the hash scratch regions, in workspace order.
+struct HashScratch {
+  size_t frag_bytes;     // split-bf16 rotation fragments
+  size_t cmax_bytes;     // per-round max column norm (float bits)
+  size_t counter_bytes;  // near-tie counter
+  size_t list_bytes;     // near-tie list (3 int32 per entry, capacity n_tokens * n_rounds)
+  size_t total;
+};
+HashScratch hash_scratch(const HashShape& s);
+
+hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const HashShape& s,
+                       int32_t* buckets, int32_t* n_near_ties, void* workspace, hipStream_t stream);
+hipError_t launch_fill_zero_buckets(int32_t* buckets, size_t n, hipStream_t stream);
+
+struct SortShape {
+  int n_seg;       // batch * heads * n_rounds
+  int seq_len;
+  int n_buckets;
+  int tile;        // positions per sort tile (one wavefront each)
+  int n_tiles;     // ceil(seq_len / tile)
+  int key_bits;    // ceil(log2(n_buckets))
+};
+SortShape make_sort_shape(int n_seg, int seq_len, int n_buckets);
+size_t sort_scratch_bytes(const SortShape& s);
+hipError_t launch_sort(const int32_t* buckets, const SortShape& s, int32_t* perm, int32_t* inv,
+                       void* workspace, hipStream_t stream);
+
+hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const int32_t* perm,
+                               int bh, int seq_len, int d, int n_rounds, int chunk_len, bool causal,
+                               float* o_rounds, float* z_rounds, hipStream_t stream);
+
+hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const void* v, bool bf16,
+                          int bh, int seq_len, int d, int n_rounds, void* out, hipStream_t stream);
+
+}  // namespace rlsh

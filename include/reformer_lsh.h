@@ -1,0 +1,191 @@
+/*
+ * reformer_lsh.h -- C ABI of the shared-QK LSH self-attention forward pass
+ * for AMD MI355X (gfx950).
+ *
+ * The operation is the Reformer's LSH attention as summarised on the page
+ * "Reformer: The Efficient Transformer" (research summary):
+ *   - Summary: queries and keys come from one shared projection, are hashed
+ *     with random rotations, sorted by bucket, and attention runs only inside
+ *     small fixed-size chunks; several hash rounds are combined.
+ *   - Key points, LSH attention bullet: h(x) = argmax([xR; -xR]) for a random
+ *     matrix R; after sorting, each chunk of m positions attends to itself and
+ *     to the chunk before it.
+ *   - Key points, Shared-QK bullet: a token is blocked from attending to
+ *     itself unless it has no other valid target.
+ *
+ * Readings taken where the page is silent (each one is also what the test
+ * oracle implements):
+ *   - rotations are float32 [n_rounds, d_head, n_buckets/2], one matrix per
+ *     round shared by every batch row and head; bucket k < b/2 is +(xR)_k and
+ *     bucket b/2 + k is -(xR)_k; argmax ties go to the lowest bucket index;
+ *     n_buckets == 1 puts every position in bucket 0 (rotations unused).
+ *   - the sort is stable: key (bucket, original position) within each
+ *     (batch, head, round).
+ *   - chunk length m' = min(chunk_len, seq_len), seq_len a multiple of m';
+ *     chunk 0 of a round has no predecessor.  Every key of the window is
+ *     eligible (no same-bucket mask).  Score s_ij = x_i . x_j / sqrt(d_head).
+ *   - causal (optional): key j is allowed for query i only if j < i in the
+ *     original order.
+ *   - a round in which a position has no valid non-self key contributes
+ *     nothing; if no round has one the output row is the position's own v.
+ *   - rounds are combined with logsumexp weights:
+ *     out_i = sum_r exp(z_r(i) - Z_i) o_r(i), Z_i = logsumexp_r z_r(i).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major memory,
+ *     owned by the caller; qk, v, out, o_rounds and workspace must be 16-byte
+ *     aligned (rows move as 16-byte vectors).  The library never allocates or frees device
+ *     memory and never synchronises; all work is enqueued in order on
+ *     `stream` (0 = the null stream).  Outputs must not alias inputs.
+ *   - Layouts: qk, v, out [batch, heads, seq_len, d_head] in `dtype`;
+ *     buckets, perm, inv_perm [batch, heads, n_rounds, seq_len] int32;
+ *     o_rounds [batch, heads, n_rounds, seq_len, d_head] float32 and
+ *     z_rounds [batch, heads, n_rounds, seq_len] float32, both indexed by
+ *     ORIGINAL position (not sorted slot).
+ *   - Arguments are validated on the host before any HIP call.  Invalid
+ *     arguments return RLSH_ERR_INVALID_ARGUMENT, shapes the kernels are not
+ *     built for return RLSH_ERR_UNSUPPORTED, a short workspace returns
+ *     RLSH_ERR_WORKSPACE_TOO_SMALL, and a failed launch returns RLSH_ERR_HIP;
+ *     in every error case nothing was enqueued (launch failures aside) and
+ *     reformer_lsh_last_error() describes the problem.  No C++ exception
+ *     crosses the ABI.
+ *   - Size limits: batch, heads, seq_len, n_rounds >= 1; d_head in {64, 128};
+ *     n_buckets == 1 or even, at most 16384; chunk_len >= 1;
+ *     batch*heads*n_rounds*seq_len < 2^31.
+ */
+#ifndef REFORMER_LSH_H
+#define REFORMER_LSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rlsh_status {
+  RLSH_OK = 0,
+  RLSH_ERR_INVALID_ARGUMENT = 1,
+  RLSH_ERR_UNSUPPORTED = 2,
+  RLSH_ERR_WORKSPACE_TOO_SMALL = 3,
+  RLSH_ERR_HIP = 4
+} rlsh_status_t;
+
+typedef enum rlsh_dtype {
+  RLSH_F32 = 0,  /* float32 qk / v / out */
+  RLSH_BF16 = 1  /* bfloat16 qk / v / out, float32 accumulation */
+} rlsh_dtype_t;
+
+/* Human-readable name of a status code (static string). */
+const char* reformer_lsh_status_string(rlsh_status_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* reformer_lsh_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int reformer_lsh_version(void);
+
+/* ---------------------------------------------------------------- hash ----
+ * Bucket ids h(x) = argmax([xR_r; -xR_r]) for every (batch, head, round,
+ * position)  (Key points, LSH attention bullet).
+ *
+ * qk         [B, H, L, d] in dtype (bf16 values are used exactly).
+ * rotations  float32 [n_rounds, d, n_buckets/2]; may be NULL if n_buckets == 1.
+ * buckets    int32 [B, H, n_rounds, L], written.
+ * workspace  device scratch of at least reformer_lsh_hash_workspace_bytes().
+ * n_near_ties (optional, may be NULL) DEVICE pointer to one int32 that
+ *            receives the number of (position, round) pairs whose float32
+ *            top-two gap was too small to trust and were re-decided in
+ *            float64 (diagnostic).
+ *
+ * Projections are computed to float32 accuracy (split-bf16 MFMA for bf16
+ * inputs, float32 FMA for float32 inputs).  Any position whose two best
+ * float32 candidates are closer than a bound on the float32 error is
+ * re-decided between those candidates in float64, so bucket ids agree with
+ * exact arithmetic except where the exact top-two gap is itself below the
+ * float32 error.
+ */
+size_t reformer_lsh_hash_workspace_bytes(int batch, int heads, int seq_len, int d_head,
+                                         int n_rounds, int n_buckets);
+rlsh_status_t reformer_lsh_hash(const void* qk, rlsh_dtype_t dtype, const float* rotations,
+                                int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                int n_buckets, int32_t* buckets, int32_t* n_near_ties,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- sort ----
+ * Stable sort of each (batch, head, round) segment by bucket id; ties keep
+ * position order (Summary: "sorted by bucket").
+ *
+ * buckets   int32 [B, H, n_rounds, L], values in [0, n_buckets) (values
+ *           outside that range are undefined behaviour).
+ * perm      int32 [B, H, n_rounds, L], written: perm[.., s] = original
+ *           position at sorted slot s.
+ * inv_perm  int32 [B, H, n_rounds, L], written: inv_perm[.., perm[.., s]] = s.
+ *           May be NULL.
+ */
+size_t reformer_lsh_sort_workspace_bytes(int batch, int heads, int seq_len, int n_rounds,
+                                         int n_buckets);
+rlsh_status_t reformer_lsh_sort(const int32_t* buckets, int batch, int heads, int seq_len,
+                                int n_rounds, int n_buckets, int32_t* perm, int32_t* inv_perm,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* -------------------------------------------------------- chunk attend ----
+ * For every round: gather the sorted rows, let each chunk of m' sorted slots
+ * attend to itself and the previous chunk with the self and (optional)
+ * causal masks, and write per-position results (Key points, LSH attention
+ * and Shared-QK bullets):
+ *   z_r(i) = log sum_{j in T_r(i)} exp(s_ij),
+ *   o_r(i) = sum_{j in T_r(i)} exp(s_ij - z_r(i)) v_j,
+ * or o_r(i) = 0, z_r(i) = -inf when T_r(i) is empty.
+ *
+ * perm      int32 [B, H, n_rounds, L], a permutation of 0..L-1 per segment
+ *           (any permutation is accepted; the sort's output is the usual one).
+ * o_rounds  float32 [B, H, n_rounds, L, d], written (position order).
+ * z_rounds  float32 [B, H, n_rounds, L], written (position order).
+ */
+rlsh_status_t reformer_lsh_chunk_attend(const void* qk, const void* v, rlsh_dtype_t dtype,
+                                        const int32_t* perm, int batch, int heads, int seq_len,
+                                        int d_head, int n_rounds, int chunk_len, int causal,
+                                        float* o_rounds, float* z_rounds, hipStream_t stream);
+
+/* ------------------------------------------------------------- combine ----
+ * out_i = sum_r exp(z_r(i) - Z_i) o_r(i), Z_i = logsumexp_r z_r(i); rows
+ * whose z_r(i) are all -inf get out_i = v_i (self fallback, Shared-QK bullet).
+ * out is written in dtype (round to nearest even for bf16).
+ */
+rlsh_status_t reformer_lsh_combine(const float* o_rounds, const float* z_rounds, const void* v,
+                                   rlsh_dtype_t dtype, int batch, int heads, int seq_len,
+                                   int d_head, int n_rounds, void* out, hipStream_t stream);
+
+/* -------------------------------------------------------------- attend ----
+ * chunk_attend followed by combine, given a permutation.  workspace holds
+ * o_rounds / z_rounds: at least reformer_lsh_attend_workspace_bytes().
+ */
+size_t reformer_lsh_attend_workspace_bytes(int batch, int heads, int seq_len, int d_head,
+                                           int n_rounds);
+rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dtype,
+                                  const int32_t* perm, int batch, int heads, int seq_len,
+                                  int d_head, int n_rounds, int chunk_len, int causal, void* out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------- attention ----
+ * The whole forward pass: hash -> sort -> chunk attention -> combine and
+ * un-sort, out [B, H, L, d] in dtype.  workspace: at least
+ * reformer_lsh_workspace_bytes() bytes (it holds buckets, perm, sort and hash
+ * scratch and the per-round o/z).
+ */
+size_t reformer_lsh_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                    int n_buckets, int chunk_len);
+rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float* rotations,
+                                     rlsh_dtype_t dtype, int batch, int heads, int seq_len,
+                                     int d_head, int n_rounds, int n_buckets, int chunk_len,
+                                     int causal, void* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REFORMER_LSH_H */
