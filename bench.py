@@ -1,0 +1,340 @@
+"""Benchmark: LSH-attention forward tokens/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload text_64k]
+
+A step is one full forward pass (hash -> sort -> chunk attention -> combine and
+un-sort) of the workload through ``reformer_lsh_attention`` on inputs already
+resident in HBM.  The default workload is the 64K-token long-text shape
+(batch 1, 8 heads, L = 65536, d = 128, 1024 buckets, chunks of 64, 4 rounds,
+causal, bf16).  Rank 0 prints one JSON line.
+
+Besides the end-to-end rate the script times every stage entry point on the
+same stream with HIP events, reports the dominant kernel against its roofline
+(algorithmic bytes or flops per launch / average launch time), and times the
+CPU oracle on a bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="text_64k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the oracle runs for cpu_baseline")
+    ap.add_argument("--quiet", action="store_true", help="only print the JSON line")
+    ap.add_argument("--profile-stage", choices=["full", "hash", "sort", "attend", "combine", "copy"],
+                    help="profiling mode: run the prerequisite stages once, then only this stage --steps times "
+                         "(copy = a plain 256 MiB device copy for counter calibration); prints its timing")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Stages:
+    """Preallocated buffers and direct C-ABI calls for each stage (marshalling only)."""
+
+    def __init__(self, nat, w, qk, v, rot):
+        import torch
+
+        self.nat, self.w, self.qk, self.v, self.rot = nat, w, qk, v, rot
+        self.lib = nat.lib()
+        B, H, L, d, r, nb = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds, w.n_buckets
+        dev = qk.device
+        self.dtype = nat._dtype_code(qk)
+        self.buckets = torch.empty((B, H, r, L), dtype=torch.int32, device=dev)
+        self.perm = torch.empty_like(self.buckets)
+        self.o = torch.empty((B, H, r, L, d), dtype=torch.float32, device=dev)
+        self.z = torch.empty((B, H, r, L), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(v)
+        self.hash_ws_n = max(1, nat.hash_workspace_bytes(B, H, L, d, r, nb))
+        self.sort_ws_n = max(1, nat.sort_workspace_bytes(B, H, L, r, nb))
+        self.full_ws_n = nat.workspace_bytes(B, H, L, d, r, nb, w.chunk_len)
+        self.hash_ws = torch.empty(self.hash_ws_n, dtype=torch.uint8, device=dev)
+        self.sort_ws = torch.empty(self.sort_ws_n, dtype=torch.uint8, device=dev)
+        self.full_ws = torch.empty(self.full_ws_n, dtype=torch.uint8, device=dev)
+        self.shape = (B, H, L, d, r, nb)
+
+    def _ok(self, st, name):
+        self.nat._check(st, name)
+
+    def stream(self):
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+
+    def full(self):
+        B, H, L, d, r, nb = self.shape
+        w = self.w
+        self._ok(self.lib.reformer_lsh_attention(self.qk.data_ptr(), self.v.data_ptr(), self.rot.data_ptr(), self.dtype,
+                                                 B, H, L, d, r, nb, w.chunk_len, int(w.causal), self.out.data_ptr(),
+                                                 self.full_ws.data_ptr(), self.full_ws_n, self.stream()),
+                 "reformer_lsh_attention")
+
+    def hash(self):
+        B, H, L, d, r, nb = self.shape
+        self._ok(self.lib.reformer_lsh_hash(self.qk.data_ptr(), self.dtype, self.rot.data_ptr(), B, H, L, d, r, nb,
+                                            self.buckets.data_ptr(), None, self.hash_ws.data_ptr(), self.hash_ws_n,
+                                            self.stream()), "reformer_lsh_hash")
+
+    def sort(self):
+        B, H, L, d, r, nb = self.shape
+        self._ok(self.lib.reformer_lsh_sort(self.buckets.data_ptr(), B, H, L, r, nb, self.perm.data_ptr(), None,
+                                            self.sort_ws.data_ptr(), self.sort_ws_n, self.stream()),
+                 "reformer_lsh_sort")
+
+    def attend(self):
+        B, H, L, d, r, nb = self.shape
+        w = self.w
+        self._ok(self.lib.reformer_lsh_chunk_attend(self.qk.data_ptr(), self.v.data_ptr(), self.dtype,
+                                                    self.perm.data_ptr(), B, H, L, d, r, w.chunk_len, int(w.causal),
+                                                    self.o.data_ptr(), self.z.data_ptr(), self.stream()),
+                 "reformer_lsh_chunk_attend")
+
+    def combine(self):
+        B, H, L, d, r, nb = self.shape
+        self._ok(self.lib.reformer_lsh_combine(self.o.data_ptr(), self.z.data_ptr(), self.v.data_ptr(), self.dtype,
+                                               B, H, L, d, r, self.out.data_ptr(), self.stream()),
+                 "reformer_lsh_combine")
+
+
+def time_calls(fn, steps, warmup):
+    """Average GPU milliseconds per call, measured with events on the launch stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def stage_work(w):
+    """Algorithmic work per launch of each stage (formulas in the design notes)."""
+    N = w.batch * w.heads * w.seq_len
+    r, d, b = w.n_rounds, w.d_head, w.n_buckets
+    e = 2 if w.dtype == "bf16" else 4
+    return {
+        # projection x.R for every head-token and round: 2 * d * (b/2) flops
+        "hash": {"flops": N * r * d * b, "bytes": N * (d * e + 4 * r)},
+        # read bucket ids twice (histogram + scatter), write perm
+        "sort": {"bytes": N * r * 12},
+        # gather qk and v rows once per round + perm, write o (fp32) and z
+        "attend": {"bytes": N * r * (2 * d * e + 4 + 4 * d + 4), "flops": N * r * 4 * min(2 * w.chunk_len, w.seq_len) * d},
+        # read o and z of every round, write out
+        "combine": {"bytes": N * (r * (4 * d + 4) + d * e)},
+    }
+
+
+KERNEL_OF_STAGE = {
+    "hash": ("hash_mfma_kernel", "efficient_long_sequence_lsh_amd/csrc/hash.hip"),
+    "sort": ("sort_scatter_kernel", "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
+    "attend": ("chunk_attend_kernel", "efficient_long_sequence_lsh_amd/csrc/attend.hip"),
+    "combine": ("combine_kernel", "efficient_long_sequence_lsh_amd/csrc/combine.hip"),
+}
+
+
+def roofline_for(stage, ms, w):
+    work = stage_work(w)[stage]
+    kernel, src = KERNEL_OF_STAGE[stage]
+    secs = ms / 1e3
+    if stage == "hash":
+        ach = work["flops"] / secs / 1e12
+        rf = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = work["bytes"] / secs / 1e9
+        rf = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(ach / HBM_PEAK_GBS, 4)}
+    rf["kernel"] = kernel
+    rf["traffic"] = measured_traffic(kernel, src, w)
+    return rf
+
+
+def measured_traffic(kernel, src, w):
+    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(w.name, {}).get(kernel)
+    if not ent or ent.get("source_sha256_16") != source_digest(os.path.join(ROOT, src)):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, heads):
+    """The float64 oracle on `heads` (batch, head) slices of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)][:heads]
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        oracle.lsh_attention_head(inp.qk[b, h].astype(np.float64), inp.v[b, h].astype(np.float64), inp.rotations,
+                                  w.n_buckets, w.chunk_len, w.causal)
+    dt = time.perf_counter() - t0
+    frac = len(pairs) / (w.batch * w.heads)       # share of one forward pass the sample covers
+    value = w.tokens * frac / dt
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = len(os.sched_getaffinity(0))
+    return {"value": round(value, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(pairs)} of {w.batch * w.heads} (batch, head) slices, full length {w.seq_len}, "
+                      f"all {w.n_rounds} rounds; {dt:.1f} s wall; value = covered share of one forward's "
+                      f"{w.tokens} tokens / wall time"}
+
+
+def profile_stage(args, st, w):
+    """Run one stage repeatedly (for rocprofv3 kernel traces and counters)."""
+    import torch
+
+    name = args.profile_stage
+    if name == "copy":
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)  # noqa: E731
+        work = {"bytes": 2 * n}
+    else:
+        if name in ("sort", "attend", "combine"):
+            st.hash()
+        if name in ("attend", "combine"):
+            st.sort()
+        if name == "combine":
+            st.attend()
+        fn = getattr(st, name)
+        work = stage_work(w).get(name, {})
+    ms = time_calls(fn, args.steps, args.warmup)
+    print(json.dumps({"profile_stage": name, "workload": w.name, "ms_per_launch": round(ms, 4),
+                      "algorithmic": work}), flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from efficient_long_sequence_lsh_amd import _native as nat
+    from efficient_long_sequence_lsh_amd import workloads as W
+
+    if not os.path.exists(nat.LIB_PATH):
+        from efficient_long_sequence_lsh_amd import build
+
+        build.build()
+    w = W.WORKLOADS[args.workload]
+    log(args, f"[bench] generating {w.name}")
+    inp = W.make_inputs(w)
+    if inp.qk_bits is not None:
+        qk = torch.from_numpy(inp.qk_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        v = torch.from_numpy(inp.v_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        qk = torch.from_numpy(inp.qk).cuda()
+        v = torch.from_numpy(inp.v).cuda()
+    rot = torch.from_numpy(inp.rotations).cuda()
+    st = Stages(nat, w, qk, v, rot)
+    if args.profile_stage:
+        profile_stage(args, st, w)
+        return
+
+    log(args, f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    for _ in range(args.warmup):
+        st.full()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(args.steps):
+        st.full()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    value = w.tokens / (ms / 1e3)
+    log(args, f"[bench] {ms:.3f} ms/step, {value:.4g} tokens/s")
+
+    stage_ms = {}
+    for name in ["hash", "sort", "attend", "combine"]:
+        stage_ms[name] = time_calls(getattr(st, name), max(5, args.steps), 2)
+        log(args, f"[bench] stage {name}: {stage_ms[name]:.4f} ms")
+    dominant = max(stage_ms, key=stage_ms.get)
+    roof = roofline_for(dominant, stage_ms[dominant], w)
+    stages = {}
+    for name, t in stage_ms.items():
+        r = roofline_for(name, t, w)
+        stages[name] = {"ms": round(t, 4), "kernel": r["kernel"], "achieved": r["achieved"], "unit": r["unit"],
+                        "frac": r["frac"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(args, f"[bench] cpu baseline: oracle on {args.cpu_heads} slices")
+        cpu = cpu_baseline(w, inp, args.cpu_heads)
+
+    line = {
+        "metric": "LSH-attention fwd tokens/sec at L=64K, 4 rounds; % of HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes and structure of the workload, no dataset)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "d_head": w.d_head,
+                   "n_buckets": w.n_buckets, "chunk_len": w.chunk_len, "n_rounds": w.n_rounds, "causal": w.causal,
+                   "qk": w.qk_kind},
+        "roofline": roof,
+        "stages": stages,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

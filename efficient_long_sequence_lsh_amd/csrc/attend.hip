@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 namespace rlsh {
 
@@ -295,6 +296,255 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(const void* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunks of exactly 64 slots (one key tile per chunk), bf16 inputs.
+//
+// A workgroup walks a run of consecutive chunks of one segment.  LDS holds two
+// chunks (K rows and transposed V): the previous chunk and the current one, so
+// every chunk is gathered from HBM once per run.  While chunk c is computed,
+// chunk c+1 is gathered into registers and written into the buffer of chunk
+// c-1 afterwards.  Query fragments come from the current chunk in LDS (the
+// queries of a chunk are its own keys).  The whole 128-key window of a query
+// fits in registers, so the softmax is single pass.  Runs are mapped to blocks
+// so that neighbouring runs share an XCD (and its L2) for the one chunk two
+// runs both read.
+constexpr int kRun64 = 16;  // chunks per workgroup
+
+template <int D>
+struct Lds64 {
+  static constexpr int kKPitch = D + 8;
+  static constexpr int kVPitch = kKTile + 4;
+  uint16_t k[2][kKTile * kKPitch];
+  uint16_t vt[2][D * kVPitch];
+  int pos[(kRun64 + 1) * kKTile];   // perm of the run's chunks (and the one before)
+};
+
+template <int D>
+struct TileRegs {
+  static constexpr int kChunks = D / 8;                  // 16-byte pieces per row
+  static constexpr int kPer = kKTile * kChunks / 256;    // pieces per thread
+  u32x4 k[kPer];
+  u32x4 v[kPer];
+};
+
+// Rows of one chunk straight from HBM into registers; positions come from LDS.
+template <int D>
+__device__ __forceinline__ void gather_tile(TileRegs<D>& t, const uint16_t* __restrict__ qk,
+                                            const uint16_t* __restrict__ vv, const int* pos, size_t row0) {
+  constexpr int kChunks = TileRegs<D>::kChunks;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kPer; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    const int row = u / kChunks, ch = u % kChunks;
+    const size_t prow = row0 + pos[row];
+    t.k[i] = *reinterpret_cast<const u32x4*>(qk + prow * D + 8 * ch);
+    t.v[i] = *reinterpret_cast<const u32x4*>(vv + prow * D + 8 * ch);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& t, Lds64<D>& sh, int buf) {
+  constexpr int kChunks = TileRegs<D>::kChunks;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kPer; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    const int row = u / kChunks, ch = u % kChunks;
+    *reinterpret_cast<u32x4*>(&sh.k[buf][row * Lds64<D>::kKPitch + 8 * ch]) = t.k[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sh.vt[buf][(8 * ch + 2 * e) * Lds64<D>::kVPitch + row] = static_cast<uint16_t>(t.v[i][e] & 0xffffu);
+      sh.vt[buf][(8 * ch + 2 * e + 1) * Lds64<D>::kVPitch + row] = static_cast<uint16_t>(t.v[i][e] >> 16);
+    }
+  }
+}
+
+// One chunk: queries = rows of buffer `cur`, keys = rows of `prv` (previous
+// chunk, if any) and `cur`.  Writes o (float32) and z by original position.
+template <int D>
+__device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int prv, bool has_prev, const int* cpos,
+                                               const int* ppos, int causal, float scale_log2, size_t orow_base,
+                                               float* __restrict__ o_rounds, float* __restrict__ z_rounds) {
+  constexpr int kKP = Lds64<D>::kKPitch;
+  constexpr int kVP = Lds64<D>::kVPitch;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q16 = lane & 15;
+  const int g = lane >> 4;
+  const int qrow = 16 * wave + q16;          // query row inside the chunk
+  const int qpos = cpos[qrow];
+  bf16x8 qf[D / 32];
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sh.k[cur][qrow * kKP + 32 * kk + 8 * g]));
+
+  // S^T for 8 subtiles of 16 keys: 0..3 previous chunk, 4..7 own chunk.
+  f32x4 sc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int buf = t < 4 ? prv : cur;
+    const int kr0 = 16 * (t & 3);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (t >= 4 || has_prev) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&sh.k[buf][(kr0 + q16) * kKP + 32 * kk + 8 * g]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], acc, 0, 0, 0);
+      }
+    }
+    sc[t] = acc;
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int* kp = t < 4 ? ppos : cpos;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kr = 16 * (t & 3) + 4 * g + j;
+      bool ok = t < 4 ? has_prev : (kr != qrow);
+      if (causal) ok = ok && (kp[kr] < qpos);
+      const float val = ok ? sc[t][j] * scale_log2 : -INFINITY;
+      sc[t][j] = val;
+      tmax = fmaxf(tmax, val);
+    }
+  }
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+  const float m_use = (tmax == -INFINITY) ? 0.0f : tmax;
+  float psum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = exp2f(sc[t][j] - m_use);
+      sc[t][j] = p;
+      psum += p;
+    }
+
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb < 2 && !has_prev) continue;
+    const int buf = kb < 2 ? prv : cur;
+    const int kb_in = kb & 1;
+    u32x4 pb;
+    pb[0] = pack_bf16x2(sc[2 * kb][0], sc[2 * kb][1]);
+    pb[1] = pack_bf16x2(sc[2 * kb][2], sc[2 * kb][3]);
+    pb[2] = pack_bf16x2(sc[2 * kb + 1][0], sc[2 * kb + 1][1]);
+    pb[3] = pack_bf16x2(sc[2 * kb + 1][2], sc[2 * kb + 1][3]);
+    const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint16_t* vrow = &sh.vt[buf][(16 * dt + q16) * kVP + 32 * kb_in + 4 * g];
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+      u32x4 a;
+      a[0] = lo[0];
+      a[1] = lo[1];
+      a[2] = hi[0];
+      a[3] = hi[1];
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bop, oacc[dt], 0, 0, 0);
+    }
+  }
+  float lsum = psum;
+  lsum += shfl_xor_f(lsum, 16);
+  lsum += shfl_xor_f(lsum, 32);
+  const bool empty = (tmax == -INFINITY) || !(lsum > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / lsum;
+  const size_t orow = orow_base + qpos;
+  float* op = o_rounds + orow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = oacc[dt][j] * inv;
+    *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = r;
+  }
+  if (g == 0) z_rounds[orow] = empty ? -INFINITY : (tmax + log2f(lsum)) * 0.69314718055994531f;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* __restrict__ qk,
+                                                             const uint16_t* __restrict__ vv,
+                                                             const int32_t* __restrict__ perm_all, AttnShape s,
+                                                             int n_seg, int runs_per_seg, int per_xcd,
+                                                             float* __restrict__ o_rounds,
+                                                             float* __restrict__ z_rounds) {
+  __shared__ Lds64<D> sh;
+  // XCD-aware mapping: hardware places block b on XCD b % 8; give each XCD a
+  // contiguous range of runs.
+  const int b = blockIdx.x;
+  const int logical = (b % 8) * per_xcd + b / 8;
+  if (logical >= n_seg * runs_per_seg) return;
+  const int seg = logical / runs_per_seg;
+  const int run = logical - seg * runs_per_seg;
+  const int bh = seg / s.n_rounds;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + static_cast<size_t>(seg) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const size_t orow_base = static_cast<size_t>(seg) * L;
+  const int c_begin = run * kRun64;
+  const int c_end = min(s.n_qt, c_begin + kRun64);
+
+  // Positions of the run's chunks: pos[(c - c_begin + 1) * 64 + row] = perm[c * 64 + row].
+  {
+    const int s_lo = (c_begin - 1) * kKTile;
+    const int s_hi = c_end * kKTile;
+    for (int i = threadIdx.x; i < (kRun64 + 1) * kKTile; i += 256) {
+      const int slot = s_lo + i;
+      sh.pos[i] = (slot >= 0 && slot < s_hi) ? perm[slot] : 0;
+    }
+  }
+  __syncthreads();
+  auto pos_of = [&](int c) -> const int* { return &sh.pos[(c - c_begin + 1) * kKTile]; };
+
+  // Register ping-pong: while chunk c is computed, chunk c+1 is already in
+  // registers (or landing) and chunk c+2 is being gathered.
+  TileRegs<D> ra, rb;
+  if (c_begin > 0) gather_tile<D>(rb, qk, vv, pos_of(c_begin - 1), row0);
+  gather_tile<D>(ra, qk, vv, pos_of(c_begin), row0);
+  if (c_begin > 0) store_tile<D>(rb, sh, 1);          // previous chunk lives in buffer 1
+  store_tile<D>(ra, sh, 0);
+  if (c_begin + 1 < c_end) gather_tile<D>(ra, qk, vv, pos_of(c_begin + 1), row0);
+  __syncthreads();
+
+  int cur = 0;
+  int c = c_begin;
+  while (true) {
+    // ra holds chunk c+1 (if any)
+    if (c + 2 < c_end) gather_tile<D>(rb, qk, vv, pos_of(c + 2), row0);
+    attend_chunk64<D>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base, o_rounds,
+                      z_rounds);
+    __syncthreads();
+    if (c + 1 < c_end) store_tile<D>(ra, sh, cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    if (++c >= c_end) break;
+    // rb holds chunk c+1 (if any)
+    if (c + 2 < c_end) gather_tile<D>(ra, qk, vv, pos_of(c + 2), row0);
+    attend_chunk64<D>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base, o_rounds,
+                      z_rounds);
+    __syncthreads();
+    if (c + 1 < c_end) store_tile<D>(rb, sh, cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    if (++c >= c_end) break;
+  }
+}
+
+template <int D>
+hipError_t launch_fast64(const void* qk, const void* v, const int32_t* perm, int n_seg, AttnShape s, float* o, float* z,
+                         hipStream_t stream) {
+  const int runs_per_seg = (s.n_qt + kRun64 - 1) / kRun64;
+  const int total = n_seg * runs_per_seg;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL(chunk_attend64_kernel<D>, dim3(8 * per_xcd), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(v), perm, s, n_seg, runs_per_seg,
+                     per_xcd, o, z);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch_typed(const void* qk, const void* v, const int32_t* perm, int n_seg, AttnShape s, float* o, float* z,
                         hipStream_t stream) {
@@ -316,6 +566,10 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
   s.causal = causal ? 1 : 0;
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   const int n_seg = bh * n_rounds;
+  if (bf16 && s.chunk == kKTile && seq_len % kKTile == 0) {
+    return d == 64 ? launch_fast64<64>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream)
+                   : launch_fast64<128>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream);
+  }
   if (d == 64) {
     return bf16 ? launch_typed<64, true>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream)
                 : launch_typed<64, false>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream);
