@@ -310,14 +310,29 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(const void* __restric
 // runs both read.
 constexpr int kRun64 = 16;  // chunks per workgroup
 
+// K and V rows are both kept row-major.  K rows are padded by 16 bytes (the
+// S^T A-operand reads of 16 rows x 16 bytes hit distinct banks); V rows by 32
+// bytes so that the transposing reads below (16 rows x 32 bytes per
+// instruction) and the 16-byte row writes are both conflict-free.
 template <int D>
 struct Lds64 {
   static constexpr int kKPitch = D + 8;
-  static constexpr int kVPitch = kKTile + 4;
+  static constexpr int kVPitch = D + 16;
   uint16_t k[2][kKTile * kKPitch];
-  uint16_t vt[2][D * kVPitch];
+  uint16_t v[2][kKTile * kVPitch];
   int pos[(kRun64 + 1) * kKTile];   // perm of the run's chunks (and the one before)
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read: within each group of 16 lanes, lane 4k+q names
+// 4 consecutive bf16 (row k, columns 4q..4q+3 of a 4x16 block) and lane i
+// receives column i, i.e. the 4 rows' values at column i.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
 
 template <int D>
 struct TileRegs {
@@ -350,11 +365,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& t, Lds64<D>& sh, i
     const int u = threadIdx.x + 256 * i;
     const int row = u / kChunks, ch = u % kChunks;
     *reinterpret_cast<u32x4*>(&sh.k[buf][row * Lds64<D>::kKPitch + 8 * ch]) = t.k[i];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sh.vt[buf][(8 * ch + 2 * e) * Lds64<D>::kVPitch + row] = static_cast<uint16_t>(t.v[i][e] & 0xffffu);
-      sh.vt[buf][(8 * ch + 2 * e + 1) * Lds64<D>::kVPitch + row] = static_cast<uint16_t>(t.v[i][e] >> 16);
-    }
+    *reinterpret_cast<u32x4*>(&sh.v[buf][row * Lds64<D>::kVPitch + 8 * ch]) = t.v[i];
   }
 }
 
@@ -434,11 +445,15 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
     pb[2] = pack_bf16x2(sc[2 * kb + 1][0], sc[2 * kb + 1][1]);
     pb[3] = pack_bf16x2(sc[2 * kb + 1][2], sc[2 * kb + 1][3]);
     const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+    // A operand (V^T, 16 features x 32 keys): lane 16g+i needs feature i of
+    // keys 32kb + 4g + {0..3} (first half) and 32kb + 16 + 4g + {0..3}
+    // (second half); lane 16g + 4k + q points at key row (.. + k), features
+    // 16dt + 4q .. +3, and the transposing read hands each lane its column.
+    const uint16_t* vbase = &sh.v[buf][(32 * kb_in + 4 * g + (q16 >> 2)) * kVP + 4 * (q16 & 3)];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const uint16_t* vrow = &sh.vt[buf][(16 * dt + q16) * kVP + 32 * kb_in + 4 * g];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+      const u32x2 lo = lds_read_tr16(vbase + 16 * dt);
+      const u32x2 hi = lds_read_tr16(vbase + 16 * kVP + 16 * dt);
       u32x4 a;
       a[0] = lo[0];
       a[1] = lo[1];
