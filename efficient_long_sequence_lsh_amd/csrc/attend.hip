@@ -57,7 +57,7 @@ template <int D, bool BF16>
 struct AttnLds;
 
 template <int D>
-struct AttnLds<D, true> {
+struct alignas(16) AttnLds<D, true> {
   static constexpr int kKPitch = D + 8;      // bf16 elements per K row (16-byte pad)
   static constexpr int kVPitch = kKTile + 4; // bf16 elements per transposed V row
   uint16_t k[kKTile * kKPitch];
@@ -66,7 +66,7 @@ struct AttnLds<D, true> {
 };
 
 template <int D>
-struct AttnLds<D, false> {
+struct alignas(16) AttnLds<D, false> {
   static constexpr int kKPitch = D + 4;      // floats per K row
   static constexpr int kVPitch = D + 4;      // floats per V row (row-major)
   float k[kKTile * kKPitch];
@@ -315,7 +315,7 @@ constexpr int kRun64 = 16;  // chunks per workgroup
 // bytes so that the transposing reads below (16 rows x 32 bytes per
 // instruction) and the 16-byte row writes are both conflict-free.
 template <int D>
-struct Lds64 {
+struct alignas(16) Lds64 {
   static constexpr int kKPitch = D + 8;
   static constexpr int kVPitch = D + 16;
   uint16_t k[2][kKTile * kKPitch];
@@ -408,11 +408,12 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int* kp = t < 4 ? ppos : cpos;
+    const u32x4 kp4 = *reinterpret_cast<const u32x4*>(kp + 16 * (t & 3) + 4 * g);   // positions of this lane's 4 keys
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kr = 16 * (t & 3) + 4 * g + j;
       bool ok = t < 4 ? has_prev : (kr != qrow);
-      if (causal) ok = ok && (kp[kr] < qpos);
+      if (causal) ok = ok && (static_cast<int>(kp4[j]) < qpos);
       const float val = ok ? sc[t][j] * scale_log2 : -INFINITY;
       sc[t][j] = val;
       tmax = fmaxf(tmax, val);
