@@ -1,6 +1,6 @@
 // C ABI of the LSH attention library: argument validation (pure host code,
 // run before any HIP call), workspace carving and the launch sequence.
-#include "../../include/reformer_lsh.h"
+#include "reformer_lsh.h"
 
 #include <stdarg.h>
 #include <stdio.h>

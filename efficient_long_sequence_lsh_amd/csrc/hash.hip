@@ -65,14 +65,20 @@ __device__ __forceinline__ float key_magnitude(uint32_t key, uint32_t code_mask)
   return __uint_as_float(((key & ~code_mask) & ~1u) >> 1);
 }
 
+// Queued (token, round) pairs live in one region per hash workgroup (capacity
+// = its tokens x rounds), counted in LDS, so no global atomic is contended.
+constexpr int kTokensPerBlock = 256;
+
 struct NearTieList {
-  int32_t* count;
+  int32_t* counts;    // per workgroup: number of queued entries
   int32_t* entries;   // 3 per entry: token, round | full<<31, c1 | c2<<16
+  int cap;            // entries per workgroup region
+  int* lds_count;     // the workgroup's counter in LDS (set inside the kernel)
 };
 
 __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int round, bool full, int c1, int c2) {
-  int idx = atomicAdd(lst.count, 1);
-  int32_t* e = lst.entries + 3 * static_cast<size_t>(idx);
+  int idx = atomicAdd(lst.lds_count, 1);
+  int32_t* e = lst.entries + 3 * (static_cast<size_t>(blockIdx.x) * lst.cap + idx);
   e[0] = tok;
   e[1] = round | (full ? static_cast<int>(0x80000000u) : 0);
   e[2] = (c1 & 0xffff) | (c2 << 16);
@@ -94,11 +100,10 @@ __device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int c
 }
 
 // ------------------------------------------------------ preparation ----
-// Zero the per-round column-norm maxima and the near-tie counter.
-__global__ void hash_init_kernel(uint32_t* cmax_bits, int n_rounds, int32_t* counter) {
-  int t = threadIdx.x;
-  if (t < n_rounds) cmax_bits[t] = 0u;
-  if (t == 0) *counter = 0;
+// Zero the per-round column-norm maxima and the caller's near-tie total.
+__global__ void hash_init_kernel(uint32_t* cmax_bits, int n_rounds, int32_t* n_near_ties) {
+  for (int t = threadIdx.x; t < n_rounds; t += blockDim.x) cmax_bits[t] = 0u;
+  if (threadIdx.x == 0 && n_near_ties != nullptr) *n_near_ties = 0;
 }
 
 // Split-bf16 fragments of R in MFMA A-operand order, plus max column norms.
@@ -158,6 +163,10 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(
   constexpr int kPerThread = kTileVec / kHashThreads;
   static_assert(kTileVec % kHashThreads == 0, "tile copy must divide evenly");
   __shared__ u32x4 lds[2][kTileVec];
+  __shared__ int ntie;
+  static_assert(kHashThreads / 64 * 32 * kStrips == kTokensPerBlock, "near-tie regions assume 256 tokens per block");
+  if (threadIdx.x == 0) ntie = 0;
+  lst.lds_count = &ntie;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -275,6 +284,7 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(
     }
     __syncthreads();
   }
+  if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
 }
 
 // ------------------------------------------------- FMA hash (float32) ----
@@ -285,6 +295,9 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
                                                        int32_t* __restrict__ buckets, NearTieList lst) {
   constexpr int kCols = 64;
   __shared__ float rt[D][kCols];
+  __shared__ int ntie;
+  if (threadIdx.x == 0) ntie = 0;
+  lst.lds_count = &ntie;
   const int tok = blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = tok < s.n_tokens;
   float x[D];
@@ -320,6 +333,8 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
                        s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
+  __syncthreads();
+  if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
 }
 
 // Column norms only (the float32 path does not need fragments).
@@ -347,13 +362,16 @@ __global__ void hash_colnorm_kernel(const float* __restrict__ rot, int half, uin
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rot,
                                                          HashShape s, int32_t* __restrict__ buckets,
-                                                         const int32_t* __restrict__ count_ptr,
-                                                         const int32_t* __restrict__ entries, int32_t* n_near_ties) {
+                                                         const int32_t* __restrict__ counts, int n_regions, int cap,
+                                                         const int32_t* __restrict__ entries_all, int32_t* n_near_ties) {
   const int lane = threadIdx.x & 63;
   const int waves = blockDim.x >> 6;
-  const int count = *count_ptr;
-  if (n_near_ties != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *n_near_ties = count;
-  for (int e = blockIdx.x * waves + (threadIdx.x >> 6); e < count; e += gridDim.x * waves) {
+  int seen = 0;
+  for (int region = blockIdx.x; region < n_regions; region += gridDim.x) {
+  const int count = counts[region];
+  seen += count;
+  const int32_t* entries = entries_all + 3 * static_cast<size_t>(region) * cap;
+  for (int e = threadIdx.x >> 6; e < count; e += waves) {
     const int tok = entries[3 * static_cast<size_t>(e)];
     const int w1 = entries[3 * static_cast<size_t>(e) + 1];
     const int w2 = entries[3 * static_cast<size_t>(e) + 2];
@@ -405,6 +423,8 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
       buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = best_b;
     }
   }
+  }
+  if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
 }
 
 __global__ void fill_zero_kernel(int32_t* p, size_t n) {
@@ -439,8 +459,9 @@ HashScratch hash_scratch(const HashShape& s) {
   HashScratch h{};
   h.frag_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * 32 * s.d * 2 * sizeof(uint16_t), 256);
   h.cmax_bytes = align_up(static_cast<size_t>(s.n_rounds) * sizeof(uint32_t), 256);
-  h.counter_bytes = 256;
-  h.list_bytes = align_up(static_cast<size_t>(s.n_tokens) * s.n_rounds * 3 * sizeof(int32_t), 256);
+  const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
+  h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
+  h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
   h.total = h.frag_bytes + h.cmax_bytes + h.counter_bytes + h.list_bytes;
   return h;
 }
@@ -458,15 +479,16 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   char* ws = static_cast<char*>(workspace);
   uint16_t* frag = reinterpret_cast<uint16_t*>(ws);
   uint32_t* cmax = reinterpret_cast<uint32_t*>(ws + h.frag_bytes);
-  int32_t* counter = reinterpret_cast<int32_t*>(ws + h.frag_bytes + h.cmax_bytes);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + h.frag_bytes + h.cmax_bytes);
   int32_t* list = reinterpret_cast<int32_t*>(ws + h.frag_bytes + h.cmax_bytes + h.counter_bytes);
-  NearTieList lst{counter, list};
+  const int n_regions = (s.n_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int cap = kTokensPerBlock * s.n_rounds;
+  NearTieList lst{counts, list, cap, nullptr};
 
-  hipLaunchKernelGGL(hash_init_kernel, dim3(1), dim3(256), 0, stream, cmax, s.n_rounds, counter);
+  hipLaunchKernelGGL(hash_init_kernel, dim3(1), dim3(256), 0, stream, cmax, s.n_rounds, n_near_ties);
   if (bf16) {
     dim3 pg(s.n_ctiles, s.n_rounds);
-    const int tokens_per_block = (kHashThreads / 64) * 32 * kStrips;
-    dim3 grid((s.n_tokens + tokens_per_block - 1) / tokens_per_block);
+    dim3 grid(n_regions);
     const uint16_t* x = static_cast<const uint16_t*>(qk);
     const u32x4* fv = reinterpret_cast<const u32x4*>(frag);
     if (s.d == 64) {
@@ -478,7 +500,7 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
     }
   } else {
     dim3 ng((s.half + 255) / 256, s.n_rounds);
-    dim3 grid((s.n_tokens + 255) / 256);
+    dim3 grid(n_regions);
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
       hipLaunchKernelGGL(hash_colnorm_kernel<64>, ng, dim3(256), 0, stream, rotations, s.half, cmax);
@@ -488,17 +510,17 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
     }
   }
-  const int fix_blocks = 1024;
+  const int fix_blocks = std::min(n_regions, 2048);
   if (s.d == 64) {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counter, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counter, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counter, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counter, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   }
   return hipGetLastError();
 }
