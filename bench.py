@@ -74,7 +74,7 @@ class Stages:
         self.out = torch.empty_like(v)
         self.hash_ws_n = max(1, nat.hash_workspace_bytes(B, H, L, d, r, nb))
         self.sort_ws_n = max(1, nat.sort_workspace_bytes(B, H, L, r, nb))
-        self.full_ws_n = nat.workspace_bytes(B, H, L, d, r, nb, w.chunk_len)
+        self.full_ws_n = nat.workspace_bytes(B, H, L, d, r, nb, w.chunk_len, self.dtype)
         self.hash_ws = torch.empty(self.hash_ws_n, dtype=torch.uint8, device=dev)
         self.sort_ws = torch.empty(self.sort_ws_n, dtype=torch.uint8, device=dev)
         self.full_ws = torch.empty(self.full_ws_n, dtype=torch.uint8, device=dev)
@@ -95,6 +95,19 @@ class Stages:
                                                  B, H, L, d, r, nb, w.chunk_len, int(w.causal), self.out.data_ptr(),
                                                  self.full_ws.data_ptr(), self.full_ws_n, self.stream()),
                  "reformer_lsh_attention")
+
+    def full_timed(self, events):
+        """The pipeline with events at its kernel boundaries (reformer_lsh_attention_timed)."""
+        import ctypes
+
+        B, H, L, d, r, nb = self.shape
+        w = self.w
+        arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+        self._ok(self.lib.reformer_lsh_attention_timed(self.qk.data_ptr(), self.v.data_ptr(), self.rot.data_ptr(),
+                                                       self.dtype, B, H, L, d, r, nb, w.chunk_len, int(w.causal),
+                                                       self.out.data_ptr(), self.full_ws.data_ptr(), self.full_ws_n,
+                                                       arr, len(events), self.stream()),
+                 "reformer_lsh_attention_timed")
 
     def hash(self):
         B, H, L, d, r, nb = self.shape
@@ -140,39 +153,54 @@ def time_calls(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def compact_rounds(w) -> bool:
+    """bf16 inputs with 64-slot chunks keep per-round results as float16 + (z, k) pairs."""
+    return w.dtype == "bf16" and min(w.chunk_len, w.seq_len) == 64 and w.seq_len % 64 == 0
+
+
 def stage_work(w):
-    """Algorithmic work per launch of each stage (formulas in the design notes)."""
+    """Algorithmic work per launch of each pipeline kernel (formulas in the design notes).
+
+    Per head-token (N = batch * heads * seq_len) and round r: the hash projects
+    onto b/2 rotation columns (2 d b/2 flops); chunk attention gathers one qk and
+    one v row plus the permutation entry and writes one o row plus its
+    normaliser; the combine reads the r rows and writes the output row.
+    """
     N = w.batch * w.heads * w.seq_len
     r, d, b = w.n_rounds, w.d_head, w.n_buckets
     e = 2 if w.dtype == "bf16" else 4
+    o_row, z_row = (2 * d, 8) if compact_rounds(w) else (4 * d, 4)
     return {
-        # projection x.R for every head-token and round: 2 * d * (b/2) flops
         "hash": {"flops": N * r * d * b, "bytes": N * (d * e + 4 * r)},
-        # read bucket ids twice (histogram + scatter), write perm
-        "sort": {"bytes": N * r * 12},
-        # gather qk and v rows once per round + perm, write o (fp32) and z
-        "attend": {"bytes": N * r * (2 * d * e + 4 + 4 * d + 4), "flops": N * r * 4 * min(2 * w.chunk_len, w.seq_len) * d},
-        # read o and z of every round, write out
-        "combine": {"bytes": N * (r * (4 * d + 4) + d * e)},
+        "sort": {"bytes": N * r * 12},   # bucket ids read by histogram and scatter, perm written
+        "attend": {"bytes": N * r * (2 * d * e + 4 + o_row + z_row),
+                   "flops": N * r * 4 * min(2 * w.chunk_len, w.seq_len) * d},
+        "combine": {"bytes": N * (r * (o_row + z_row) + d * e)},
     }
 
 
-KERNEL_OF_STAGE = {
-    "hash": ("hash_mfma_kernel", "efficient_long_sequence_lsh_amd/csrc/hash.hip"),
-    "sort": ("sort_scatter_kernel", "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
-    "attend": ("chunk_attend_kernel", "efficient_long_sequence_lsh_amd/csrc/attend.hip"),
-    "combine": ("combine_kernel", "efficient_long_sequence_lsh_amd/csrc/combine.hip"),
-}
+def kernel_of_stage(w):
+    attend = "chunk_attend64_kernel" if w.dtype == "bf16" and min(w.chunk_len, w.seq_len) == 64 else "chunk_attend_kernel"
+    combine = "combine_compact_kernel" if compact_rounds(w) else "combine_kernel"
+    hash_k = "hash_mfma_kernel" if w.dtype == "bf16" else "hash_fma_kernel"
+    return {
+        "hash": (hash_k, "efficient_long_sequence_lsh_amd/csrc/hash.hip"),
+        "sort": ("sort_hist_kernel+sort_scan*+sort_scatter_kernel", "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
+        "attend": (attend, "efficient_long_sequence_lsh_amd/csrc/attend.hip"),
+        "combine": (combine, "efficient_long_sequence_lsh_amd/csrc/combine.hip"),
+    }
 
 
 def roofline_for(stage, ms, w):
     work = stage_work(w)[stage]
-    kernel, src = KERNEL_OF_STAGE[stage]
+    kernel, src = kernel_of_stage(w)[stage]
     secs = ms / 1e3
     if stage == "hash":
         ach = work["flops"] / secs / 1e12
         rf = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-              "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+              "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+              # float32-accurate projections run as two bf16 MFMA passes (R = R_hi + R_lo)
+              "executed_mfma_frac": round(2 * ach / MFMA_BF16_PEAK_TFLOPS, 4)}
     else:
         ach = work["bytes"] / secs / 1e9
         rf = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -296,17 +324,33 @@ def main():
     value = w.tokens / (ms / 1e3)
     log(args, f"[bench] {ms:.3f} ms/step, {value:.4g} tokens/s")
 
-    stage_ms = {}
-    for name in ["hash", "sort", "attend", "combine"]:
-        stage_ms[name] = time_calls(getattr(st, name), max(5, args.steps), 2)
-        log(args, f"[bench] stage {name}: {stage_ms[name]:.4f} ms")
-    dominant = max(stage_ms, key=stage_ms.get)
+    # Per-kernel durations of the pipeline's own launches: HIP events recorded
+    # by the library at its kernel boundaries on this stream, every timed step.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(nat.TIMED_EVENTS)]
+    for ev in events:
+        ev.record()                       # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    spans = {"hash_setup": (0, 1), "hash": (1, 2), "hash_fixup": (2, 3), "sort": (3, 4), "attend": (4, 5),
+             "combine": (5, 6)}
+    acc = {k: 0.0 for k in spans}
+    for _ in range(args.steps):
+        st.full_timed(events)
+        torch.cuda.synchronize()
+        for k, (a, b) in spans.items():
+            acc[k] += events[a].elapsed_time(events[b])
+    stage_ms = {k: v / args.steps for k, v in acc.items()}
+    for k, v in stage_ms.items():
+        log(args, f"[bench] {k}: {v:.4f} ms")
+    main = ["hash", "sort", "attend", "combine"]
+    dominant = max(main, key=lambda k: stage_ms[k])
     roof = roofline_for(dominant, stage_ms[dominant], w)
     stages = {}
-    for name, t in stage_ms.items():
-        r = roofline_for(name, t, w)
-        stages[name] = {"ms": round(t, 4), "kernel": r["kernel"], "achieved": r["achieved"], "unit": r["unit"],
-                        "frac": r["frac"]}
+    for name in main:
+        r = roofline_for(name, stage_ms[name], w)
+        stages[name] = {"ms": round(stage_ms[name], 4), "kernel": r["kernel"], "achieved": r["achieved"],
+                        "unit": r["unit"], "frac": r["frac"]}
+    stages["hash_setup"] = {"ms": round(stage_ms["hash_setup"], 4)}
+    stages["hash_fixup"] = {"ms": round(stage_ms["hash_fixup"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

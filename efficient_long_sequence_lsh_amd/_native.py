@@ -36,11 +36,14 @@ SIGNATURES = {
     "reformer_lsh_sort": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]),
     "reformer_lsh_chunk_attend": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "reformer_lsh_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]),
-    "reformer_lsh_attend_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "reformer_lsh_attend_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "reformer_lsh_attend": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
-    "reformer_lsh_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "reformer_lsh_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "reformer_lsh_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
+    "reformer_lsh_attention_timed": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p, _i, _p]),
 }
+
+TIMED_EVENTS = 7   # RLSH_TIMED_EVENTS
 
 _lib = None
 
@@ -174,7 +177,7 @@ def attend(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk_len: int
     _check_pair(qk, v)
     B, H, L, d = qk.shape
     r = perm.shape[2]
-    nbytes = int(lib().reformer_lsh_attend_workspace_bytes(B, H, L, d, r))
+    nbytes = int(lib().reformer_lsh_attend_workspace_bytes(_dtype_code(qk), B, H, L, d, r, int(chunk_len)))
     ws = _ws(nbytes, qk.device)
     out = torch.empty_like(v)
     st = lib().reformer_lsh_attend(_dev(qk, "qk"), _dev(v, "v"), _dtype_code(qk), _dev(perm, "perm"), B, H, L, d, r,
@@ -183,8 +186,12 @@ def attend(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk_len: int
     return out
 
 
-def workspace_bytes(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len) -> int:
-    return int(lib().reformer_lsh_workspace_bytes(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len))
+def workspace_bytes(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len, dtype=RLSH_BF16) -> int:
+    """Workspace of reformer_lsh_attention; dtype is RLSH_F32 / RLSH_BF16 (or a torch dtype)."""
+    if not isinstance(dtype, int):
+        dtype = RLSH_BF16 if dtype == torch.bfloat16 else RLSH_F32
+    return int(lib().reformer_lsh_workspace_bytes(dtype, batch, heads, seq_len, d_head, n_rounds, n_buckets,
+                                                  chunk_len))
 
 
 def attention(qk: torch.Tensor, v: torch.Tensor, rotations: torch.Tensor | None, n_buckets: int, chunk_len: int,
@@ -202,7 +209,7 @@ def attention(qk: torch.Tensor, v: torch.Tensor, rotations: torch.Tensor | None,
         if rotations is None or rotations.dtype != torch.float32 or tuple(rotations.shape) != (n_rounds, d, n_buckets // 2):
             raise ValueError("rotations must be float32 [n_rounds, d, n_buckets/2]")
         rot_ptr = _dev(rotations, "rotations")
-    nbytes = workspace_bytes(B, H, L, d, n_rounds, n_buckets, chunk_len)
+    nbytes = workspace_bytes(B, H, L, d, n_rounds, n_buckets, chunk_len, _dtype_code(qk))
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = _ws(nbytes, qk.device)
     if out is None:

@@ -91,29 +91,73 @@ size_t sort_ws(int batch, int heads, int seq_len, int n_rounds, int n_buckets) {
   return rlsh::sort_scratch_bytes(rlsh::make_sort_shape(batch * heads * n_rounds, seq_len, n_buckets));
 }
 
-size_t attend_ws(int batch, int heads, int seq_len, int d_head, int n_rounds) {
+// Per-round intermediates: float32 o and z, or (bf16 inputs with 64-slot
+// chunks) float16 o scaled per row plus (z, k) float pairs.
+struct RoundLayout {
+  bool compact;
+  size_t o_bytes, z_bytes;
+};
+
+RoundLayout round_layout(rlsh_dtype_t dtype, int batch, int heads, int seq_len, int d_head, int n_rounds,
+                         int chunk_len) {
   const size_t n = tokens(batch, heads, seq_len) * n_rounds;
-  return a256(n * d_head * sizeof(float)) + a256(n * sizeof(float));
+  RoundLayout r{};
+  r.compact = rlsh::compact_rounds_supported(dtype == RLSH_BF16, seq_len, chunk_len);
+  r.o_bytes = a256(n * d_head * (r.compact ? sizeof(uint16_t) : sizeof(float)));
+  r.z_bytes = a256(n * (r.compact ? sizeof(float2) : sizeof(float)));
+  return r;
 }
 
-// Full pipeline layout: buckets | perm | region (o_rounds, aliased earlier by
-// the hash and sort scratch, which are dead once attention starts) | z_rounds.
+size_t attend_ws(rlsh_dtype_t dtype, int batch, int heads, int seq_len, int d_head, int n_rounds, int chunk_len) {
+  const RoundLayout r = round_layout(dtype, batch, heads, seq_len, d_head, n_rounds, chunk_len);
+  return r.o_bytes + r.z_bytes;
+}
+
+// Full pipeline layout: buckets | perm | region (per-round o, aliased earlier
+// by the hash and sort scratch, which are dead once attention starts) | z.
 struct FullLayout {
+  RoundLayout rounds;
   size_t buckets, perm, region, z, total;
 };
 
-FullLayout full_layout(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets) {
+FullLayout full_layout(rlsh_dtype_t dtype, int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                       int chunk_len) {
   const size_t n = tokens(batch, heads, seq_len) * n_rounds;
   FullLayout f{};
+  f.rounds = round_layout(dtype, batch, heads, seq_len, d_head, n_rounds, chunk_len);
   f.buckets = 0;
   f.perm = a256(n * sizeof(int32_t));
-  size_t region = a256(n * d_head * sizeof(float));
+  size_t region = f.rounds.o_bytes;
   region = std::max(region, a256(hash_ws(batch, heads, seq_len, d_head, n_rounds, n_buckets)));
   region = std::max(region, a256(sort_ws(batch, heads, seq_len, n_rounds, n_buckets)));
   f.region = f.perm + a256(n * sizeof(int32_t));
   f.z = f.region + region;
-  f.total = f.z + a256(n * sizeof(float));
+  f.total = f.z + f.rounds.z_bytes;
   return f;
+}
+
+// chunk attention + combine into `out`, with the intermediates at o_mem / z_mem.
+// mark (optional): event recorded between the two kernels.
+hipError_t run_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int bh, int seq_len,
+                      int d_head, int n_rounds, int chunk_len, int causal, void* out, const RoundLayout& rl,
+                      void* o_mem, void* z_mem, hipStream_t stream, hipEvent_t* mark = nullptr) {
+  const bool bf16 = dtype == RLSH_BF16;
+  hipError_t e;
+  if (rl.compact) {
+    uint16_t* o16 = static_cast<uint16_t*>(o_mem);
+    float2* zk = static_cast<float2*>(z_mem);
+    e = rlsh::launch_chunk_attend_compact(qk, v, perm, bh, seq_len, d_head, n_rounds, causal != 0, o16, zk, stream);
+    if (e == hipSuccess && mark) e = hipEventRecord(*mark, stream);
+    if (e == hipSuccess) e = rlsh::launch_combine_compact(o16, zk, v, bh, seq_len, d_head, n_rounds, out, stream);
+  } else {
+    float* o = static_cast<float*>(o_mem);
+    float* z = static_cast<float*>(z_mem);
+    e = rlsh::launch_chunk_attend(qk, v, bf16, perm, bh, seq_len, d_head, n_rounds, chunk_len, causal != 0, o, z,
+                                  stream);
+    if (e == hipSuccess && mark) e = hipEventRecord(*mark, stream);
+    if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, bh, seq_len, d_head, n_rounds, out, stream);
+  }
+  return e;
 }
 
 }  // namespace
@@ -217,9 +261,11 @@ rlsh_status_t reformer_lsh_combine(const float* o_rounds, const float* z_rounds,
                     "reformer_lsh_combine");
 }
 
-size_t reformer_lsh_attend_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds) {
-  if (check_shape(batch, heads, seq_len, d_head, n_rounds, -1, -1) != RLSH_OK) return 0;
-  return attend_ws(batch, heads, seq_len, d_head, n_rounds);
+size_t reformer_lsh_attend_workspace_bytes(rlsh_dtype_t dtype, int batch, int heads, int seq_len, int d_head,
+                                           int n_rounds, int chunk_len) {
+  if (check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len) != RLSH_OK) return 0;
+  if (check_dtype(dtype) != RLSH_OK) return 0;
+  return attend_ws(dtype, batch, heads, seq_len, d_head, n_rounds, chunk_len);
 }
 
 rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int batch,
@@ -233,29 +279,27 @@ rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dt
   if ((st = check_aligned(qk, "qk")) != RLSH_OK || (st = check_aligned(v, "v")) != RLSH_OK ||
       (st = check_aligned(out, "out")) != RLSH_OK || (st = check_aligned(workspace, "workspace")) != RLSH_OK)
     return st;
-  const size_t need = attend_ws(batch, heads, seq_len, d_head, n_rounds);
+  const RoundLayout rl = round_layout(dtype, batch, heads, seq_len, d_head, n_rounds, chunk_len);
+  const size_t need = rl.o_bytes + rl.z_bytes;
   if (workspace == nullptr || workspace_bytes < need)
     return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "attend workspace needs %zu bytes (got %zu)", need, workspace_bytes);
-  const size_t n = tokens(batch, heads, seq_len) * n_rounds;
-  float* o = static_cast<float*>(workspace);
-  float* z = reinterpret_cast<float*>(static_cast<char*>(workspace) + a256(n * d_head * sizeof(float)));
-  const bool bf16 = dtype == RLSH_BF16;
-  hipError_t e = rlsh::launch_chunk_attend(qk, v, bf16, perm, batch * heads, seq_len, d_head, n_rounds, chunk_len,
-                                           causal != 0, o, z, stream);
-  if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, batch * heads, seq_len, d_head, n_rounds, out, stream);
-  return hip_status(e, "reformer_lsh_attend");
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(run_attend(qk, v, dtype, perm, batch * heads, seq_len, d_head, n_rounds, chunk_len, causal, out, rl,
+                               ws, ws + rl.o_bytes, stream),
+                    "reformer_lsh_attend");
 }
 
-size_t reformer_lsh_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
-                                    int chunk_len) {
+size_t reformer_lsh_workspace_bytes(rlsh_dtype_t dtype, int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                    int n_buckets, int chunk_len) {
   if (check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len) != RLSH_OK) return 0;
-  return full_layout(batch, heads, seq_len, d_head, n_rounds, n_buckets).total;
+  if (check_dtype(dtype) != RLSH_OK) return 0;
+  return full_layout(dtype, batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len).total;
 }
 
-rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float* rotations, rlsh_dtype_t dtype,
-                                     int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
-                                     int chunk_len, int causal, void* out, void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
+static rlsh_status_t attention_impl(const void* qk, const void* v, const float* rotations, rlsh_dtype_t dtype,
+                                    int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                                    int chunk_len, int causal, void* out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, hipEvent_t* ev) {
   rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len);
   if (st != RLSH_OK) return st;
   if ((st = check_dtype(dtype)) != RLSH_OK) return st;
@@ -266,34 +310,57 @@ rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float*
     return st;
   if (n_buckets > 1 && rotations == nullptr)
     return fail(RLSH_ERR_INVALID_ARGUMENT, "rotations must be non-null when n_buckets > 1");
-  const FullLayout f = full_layout(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+  const FullLayout f = full_layout(dtype, batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len);
   if (workspace == nullptr || workspace_bytes < f.total)
     return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", f.total, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
   int32_t* bk = reinterpret_cast<int32_t*>(ws + f.buckets);
   int32_t* perm = reinterpret_cast<int32_t*>(ws + f.perm);
   void* region = ws + f.region;
-  float* o = reinterpret_cast<float*>(region);
-  float* z = reinterpret_cast<float*>(ws + f.z);
   const bool bf16 = dtype == RLSH_BF16;
   const int bh = batch * heads;
   hipError_t e = hipSuccess;
-  if (n_buckets > 1) {
+  if (ev) e = hipEventRecord(ev[0], stream);
+  if (e == hipSuccess && n_buckets > 1) {
     const rlsh::HashShape hs = rlsh::make_hash_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets);
-    e = rlsh::launch_hash(qk, bf16, rotations, hs, bk, nullptr, region, stream);
+    e = rlsh::launch_hash(qk, bf16, rotations, hs, bk, nullptr, region, stream, ev ? ev + 1 : nullptr);
     if (e == hipSuccess) {
       const rlsh::SortShape ss = rlsh::make_sort_shape(bh * n_rounds, seq_len, n_buckets);
       e = rlsh::launch_sort(bk, ss, perm, nullptr, region, stream);
     }
-  } else {
+  } else if (e == hipSuccess) {
     // One bucket: every round keeps the original order.
+    for (int i = 1; ev && e == hipSuccess && i <= 3; ++i) e = hipEventRecord(ev[i], stream);
     const rlsh::SortShape ss = rlsh::make_sort_shape(bh * n_rounds, seq_len, 1);
-    e = rlsh::launch_sort(nullptr, ss, perm, nullptr, nullptr, stream);
+    if (e == hipSuccess) e = rlsh::launch_sort(nullptr, ss, perm, nullptr, nullptr, stream);
   }
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[4], stream);
   if (e == hipSuccess)
-    e = rlsh::launch_chunk_attend(qk, v, bf16, perm, bh, seq_len, d_head, n_rounds, chunk_len, causal != 0, o, z, stream);
-  if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, bh, seq_len, d_head, n_rounds, out, stream);
+    e = run_attend(qk, v, dtype, perm, bh, seq_len, d_head, n_rounds, chunk_len, causal, out, f.rounds, region,
+                   ws + f.z, stream, ev ? ev + 5 : nullptr);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[6], stream);
   return hip_status(e, "reformer_lsh_attention");
+}
+
+rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float* rotations, rlsh_dtype_t dtype,
+                                     int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                                     int chunk_len, int causal, void* out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  return attention_impl(qk, v, rotations, dtype, batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len,
+                        causal, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+rlsh_status_t reformer_lsh_attention_timed(const void* qk, const void* v, const float* rotations, rlsh_dtype_t dtype,
+                                           int batch, int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                                           int chunk_len, int causal, void* out, void* workspace,
+                                           size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                           hipStream_t stream) {
+  if (events == nullptr || n_events < RLSH_TIMED_EVENTS)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "events must hold %d hipEvent_t", RLSH_TIMED_EVENTS);
+  for (int i = 0; i < RLSH_TIMED_EVENTS; ++i)
+    if (events[i] == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "events[%d] is null", i);
+  return attention_impl(qk, v, rotations, dtype, batch, heads, seq_len, d_head, n_rounds, n_buckets, chunk_len,
+                        causal, out, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

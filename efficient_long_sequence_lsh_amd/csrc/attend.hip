@@ -369,12 +369,24 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& t, Lds64<D>& sh, i
   }
 }
 
+// Where a round's per-position results go.  Plain: o float32 [.., d] and z
+// float32.  Compact (bf16 inputs inside the pipeline): o as float16 scaled by
+// 2^-k per row (k = 0 unless the row's largest magnitude reaches 2^15) and
+// (z, k) as a float pair; this halves the bytes of the largest intermediate
+// while keeping 11 significant bits.
+struct RoundSink {
+  float* o;          // plain
+  float* z;          // plain
+  uint16_t* o16;     // compact
+  float2* zk;        // compact
+};
+
 // One chunk: queries = rows of buffer `cur`, keys = rows of `prv` (previous
-// chunk, if any) and `cur`.  Writes o (float32) and z by original position.
-template <int D>
+// chunk, if any) and `cur`.  Writes o and z by original position.
+template <int D, bool O16>
 __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int prv, bool has_prev, const int* cpos,
                                                const int* ppos, int causal, float scale_log2, size_t orow_base,
-                                               float* __restrict__ o_rounds, float* __restrict__ z_rounds) {
+                                               RoundSink out) {
   constexpr int kKP = Lds64<D>::kKPitch;
   constexpr int kVP = Lds64<D>::kVPitch;
   const int lane = threadIdx.x & 63;
@@ -469,24 +481,55 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
   const bool empty = (tmax == -INFINITY) || !(lsum > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / lsum;
   const size_t orow = orow_base + qpos;
-  float* op = o_rounds + orow * D;
+  const float zval = empty ? -INFINITY : (tmax + log2f(lsum)) * 0.69314718055994531f;
+  if constexpr (!O16) {
+    float* op = out.o + orow * D;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    f32x4 r;
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = oacc[dt][j] * inv;
-    *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = r;
+      for (int j = 0; j < 4; ++j) r[j] = oacc[dt][j] * inv;
+      *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = r;
+    }
+    if (g == 0) out.z[orow] = zval;
+  } else {
+    // Row maximum (the row is spread over the 4 lanes q16 + 16g).
+    float amax = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(oacc[dt][j] * inv));
+    amax = fmaxf(amax, shfl_xor_f(amax, 16));
+    amax = fmaxf(amax, shfl_xor_f(amax, 32));
+    // k = 0 for rows inside the float16 range, else the smallest k with
+    // amax * 2^-k < 2^15 (exponent arithmetic on the float bits).
+    const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+    const int k = e >= 15 ? e - 14 : 0;
+    const float down = __uint_as_float(static_cast<uint32_t>(127 - k) << 23) * inv;   // 2^-k / lsum
+    uint16_t* op = out.o16 + orow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      u32x2 pk;
+      const _Float16 h0 = static_cast<_Float16>(oacc[dt][0] * down);
+      const _Float16 h1 = static_cast<_Float16>(oacc[dt][1] * down);
+      const _Float16 h2 = static_cast<_Float16>(oacc[dt][2] * down);
+      const _Float16 h3 = static_cast<_Float16>(oacc[dt][3] * down);
+      pk[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+      pk[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) |
+              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
+      *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = pk;
+    }
+    if (g == 0) out.zk[orow] = make_float2(zval, static_cast<float>(k));
   }
-  if (g == 0) z_rounds[orow] = empty ? -INFINITY : (tmax + log2f(lsum)) * 0.69314718055994531f;
 }
 
-template <int D>
+template <int D, bool O16>
 __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* __restrict__ qk,
-                                                             const uint16_t* __restrict__ vv,
-                                                             const int32_t* __restrict__ perm_all, AttnShape s,
-                                                             int n_seg, int runs_per_seg, int per_xcd,
-                                                             float* __restrict__ o_rounds,
-                                                             float* __restrict__ z_rounds) {
+                                                                const uint16_t* __restrict__ vv,
+                                                                const int32_t* __restrict__ perm_all, AttnShape s,
+                                                                int n_seg, int runs_per_seg, int per_xcd,
+                                                                RoundSink out) {
   __shared__ Lds64<D> sh;
   // XCD-aware mapping: hardware places block b on XCD b % 8; give each XCD a
   // contiguous range of runs.
@@ -530,8 +573,8 @@ __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* 
   while (true) {
     // ra holds chunk c+1 (if any)
     if (c + 2 < c_end) gather_tile<D>(rb, qk, vv, pos_of(c + 2), row0);
-    attend_chunk64<D>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base, o_rounds,
-                      z_rounds);
+    attend_chunk64<D, O16>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base,
+                           out);
     __syncthreads();
     if (c + 1 < c_end) store_tile<D>(ra, sh, cur ^ 1);
     __syncthreads();
@@ -539,8 +582,8 @@ __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* 
     if (++c >= c_end) break;
     // rb holds chunk c+1 (if any)
     if (c + 2 < c_end) gather_tile<D>(ra, qk, vv, pos_of(c + 2), row0);
-    attend_chunk64<D>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base, o_rounds,
-                      z_rounds);
+    attend_chunk64<D, O16>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base,
+                           out);
     __syncthreads();
     if (c + 1 < c_end) store_tile<D>(rb, sh, cur ^ 1);
     __syncthreads();
@@ -549,15 +592,15 @@ __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* 
   }
 }
 
-template <int D>
-hipError_t launch_fast64(const void* qk, const void* v, const int32_t* perm, int n_seg, AttnShape s, float* o, float* z,
+template <int D, bool O16>
+hipError_t launch_fast64(const void* qk, const void* v, const int32_t* perm, int n_seg, AttnShape s, RoundSink out,
                          hipStream_t stream) {
   const int runs_per_seg = (s.n_qt + kRun64 - 1) / kRun64;
   const int total = n_seg * runs_per_seg;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(chunk_attend64_kernel<D>, dim3(8 * per_xcd), dim3(256), 0, stream,
+  hipLaunchKernelGGL((chunk_attend64_kernel<D, O16>), dim3(8 * per_xcd), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(v), perm, s, n_seg, runs_per_seg,
-                     per_xcd, o, z);
+                     per_xcd, out);
   return hipGetLastError();
 }
 
@@ -583,8 +626,9 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   const int n_seg = bh * n_rounds;
   if (bf16 && s.chunk == kKTile && seq_len % kKTile == 0) {
-    return d == 64 ? launch_fast64<64>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream)
-                   : launch_fast64<128>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream);
+    RoundSink out{o_rounds, z_rounds, nullptr, nullptr};
+    return d == 64 ? launch_fast64<64, false>(qk, v, perm, n_seg, s, out, stream)
+                   : launch_fast64<128, false>(qk, v, perm, n_seg, s, out, stream);
   }
   if (d == 64) {
     return bf16 ? launch_typed<64, true>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream)
@@ -592,6 +636,25 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
   }
   return bf16 ? launch_typed<128, true>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream)
               : launch_typed<128, false>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream);
+}
+
+bool compact_rounds_supported(bool bf16, int seq_len, int chunk_len) {
+  return bf16 && std::min(chunk_len, seq_len) == kKTile && seq_len % kKTile == 0;
+}
+
+hipError_t launch_chunk_attend_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len, int d,
+                                       int n_rounds, bool causal, uint16_t* o16, float2* zk, hipStream_t stream) {
+  AttnShape s{};
+  s.seq_len = seq_len;
+  s.chunk = kKTile;
+  s.n_rounds = n_rounds;
+  s.n_qt = seq_len / kKTile;
+  s.causal = causal ? 1 : 0;
+  s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+  RoundSink out{nullptr, nullptr, o16, zk};
+  const int n_seg = bh * n_rounds;
+  return d == 64 ? launch_fast64<64, true>(qk, v, perm, n_seg, s, out, stream)
+                 : launch_fast64<128, true>(qk, v, perm, n_seg, s, out, stream);
 }
 
 }  // namespace rlsh

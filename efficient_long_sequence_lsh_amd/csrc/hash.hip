@@ -474,7 +474,7 @@ hipError_t launch_fill_zero_buckets(int32_t* buckets, size_t n, hipStream_t stre
 }
 
 hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const HashShape& s, int32_t* buckets,
-                       int32_t* n_near_ties, void* workspace, hipStream_t stream) {
+                       int32_t* n_near_ties, void* workspace, hipStream_t stream, hipEvent_t* marks) {
   HashScratch h = hash_scratch(s);
   char* ws = static_cast<char*>(workspace);
   uint16_t* frag = reinterpret_cast<uint16_t*>(ws);
@@ -493,9 +493,11 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
     const u32x4* fv = reinterpret_cast<const u32x4*>(frag);
     if (s.d == 64) {
       hipLaunchKernelGGL(hash_prepare_kernel<64>, pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, cmax);
+      if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, fv, cmax, s, buckets, lst);
     } else {
       hipLaunchKernelGGL(hash_prepare_kernel<128>, pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, cmax);
+      if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, fv, cmax, s, buckets, lst);
     }
   } else {
@@ -504,12 +506,15 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
       hipLaunchKernelGGL(hash_colnorm_kernel<64>, ng, dim3(256), 0, stream, rotations, s.half, cmax);
+      if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
     } else {
       hipLaunchKernelGGL(hash_colnorm_kernel<128>, ng, dim3(256), 0, stream, rotations, s.half, cmax);
+      if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
     }
   }
+  if (marks) (void)hipEventRecord(marks[1], stream);
   const int fix_blocks = std::min(n_regions, 2048);
   if (s.d == 64) {
     if (bf16)
@@ -522,6 +527,7 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
     else
       hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   }
+  if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();
 }
 

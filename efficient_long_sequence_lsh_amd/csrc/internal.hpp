@@ -31,8 +31,11 @@ struct HashScratch {
 };
 HashScratch hash_scratch(const HashShape& s);
 
+// marks (optional, may be null): events recorded after the set-up kernels, after the
+// projection/argmax kernel and after the near-tie fix-up.
 hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const HashShape& s,
-                       int32_t* buckets, int32_t* n_near_ties, void* workspace, hipStream_t stream);
+                       int32_t* buckets, int32_t* n_near_ties, void* workspace, hipStream_t stream,
+                       hipEvent_t* marks = nullptr);
 hipError_t launch_fill_zero_buckets(int32_t* buckets, size_t n, hipStream_t stream);
 
 struct SortShape {
@@ -54,5 +57,13 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
 
 hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const void* v, bool bf16,
                           int bh, int seq_len, int d, int n_rounds, void* out, hipStream_t stream);
+
+// Compact per-round intermediates for the bf16 pipeline with 64-slot chunks:
+// o as float16 scaled by 2^-k per row, (z, k) as float pairs.
+bool compact_rounds_supported(bool bf16, int seq_len, int chunk_len);
+hipError_t launch_chunk_attend_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len, int d,
+                                       int n_rounds, bool causal, uint16_t* o16, float2* zk, hipStream_t stream);
+hipError_t launch_combine_compact(const uint16_t* o16, const float2* zk, const void* v, int bh, int seq_len, int d,
+                                  int n_rounds, void* out, hipStream_t stream);
 
 }  // namespace rlsh

@@ -160,11 +160,14 @@ rlsh_status_t reformer_lsh_combine(const float* o_rounds, const float* z_rounds,
                                    int d_head, int n_rounds, void* out, hipStream_t stream);
 
 /* -------------------------------------------------------------- attend ----
- * chunk_attend followed by combine, given a permutation.  workspace holds
- * o_rounds / z_rounds: at least reformer_lsh_attend_workspace_bytes().
+ * chunk_attend followed by combine, given a permutation.  workspace holds the
+ * per-round results: at least reformer_lsh_attend_workspace_bytes().  For
+ * bf16 inputs with 64-slot chunks the workspace keeps them compact (o as
+ * float16 scaled by a per-row power of two, 11 significant bits); otherwise
+ * as float32 (the layout of reformer_lsh_chunk_attend).
  */
-size_t reformer_lsh_attend_workspace_bytes(int batch, int heads, int seq_len, int d_head,
-                                           int n_rounds);
+size_t reformer_lsh_attend_workspace_bytes(rlsh_dtype_t dtype, int batch, int heads, int seq_len,
+                                           int d_head, int n_rounds, int chunk_len);
 rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dtype,
                                   const int32_t* perm, int batch, int heads, int seq_len,
                                   int d_head, int n_rounds, int chunk_len, int causal, void* out,
@@ -176,13 +179,33 @@ rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dt
  * reformer_lsh_workspace_bytes() bytes (it holds buckets, perm, sort and hash
  * scratch and the per-round o/z).
  */
-size_t reformer_lsh_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds,
-                                    int n_buckets, int chunk_len);
+size_t reformer_lsh_workspace_bytes(rlsh_dtype_t dtype, int batch, int heads, int seq_len,
+                                    int d_head, int n_rounds, int n_buckets, int chunk_len);
 rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float* rotations,
                                      rlsh_dtype_t dtype, int batch, int heads, int seq_len,
                                      int d_head, int n_rounds, int n_buckets, int chunk_len,
                                      int causal, void* out, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------- instrumentation ----
+ * reformer_lsh_attention with hipEventRecord calls at kernel boundaries, for
+ * measuring the launches of the real pipeline on the caller's stream.
+ * events: RLSH_TIMED_EVENTS caller-created events (hipEventCreate), recorded on
+ * `stream` in this order:
+ *   0 start            1 after the hash set-up kernels (rotation preparation)
+ *   2 after the projection/argmax kernel       3 after the near-tie fix-up
+ *   4 after the sort   5 after chunk attention 6 after the round combine
+ * (with n_buckets == 1 events 1..3 are recorded where the hash would run).
+ * Arguments and errors otherwise as reformer_lsh_attention; a null events
+ * array or fewer than RLSH_TIMED_EVENTS entries is RLSH_ERR_INVALID_ARGUMENT.
+ */
+#define RLSH_TIMED_EVENTS 7
+rlsh_status_t reformer_lsh_attention_timed(const void* qk, const void* v, const float* rotations,
+                                           rlsh_dtype_t dtype, int batch, int heads, int seq_len,
+                                           int d_head, int n_rounds, int n_buckets, int chunk_len,
+                                           int causal, void* out, void* workspace,
+                                           size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -91,14 +91,19 @@ def test_stage_entry_points_reject_bad_arguments(lib):
 
 
 def test_workspace_sizes(lib):
-    full = lib.reformer_lsh_workspace_bytes(1, 8, 65536, 128, 4, 1024, 64)
     n = 8 * 65536 * 4
-    assert full >= n * 128 * 4 + n * 4 * 3      # o + z + buckets + perm
-    assert full < n * 128 * 4 * 1.2
-    assert lib.reformer_lsh_workspace_bytes(1, 8, 65536, 96, 4, 1024, 64) == 0   # invalid -> 0
+    full32 = lib.reformer_lsh_workspace_bytes(0, 1, 8, 65536, 128, 4, 1024, 64)
+    assert full32 >= n * 128 * 4 + n * 4 * 3      # float32 o + z + buckets + perm
+    assert full32 < n * 128 * 4 * 1.2
+    full16 = lib.reformer_lsh_workspace_bytes(1, 1, 8, 65536, 128, 4, 1024, 64)
+    assert n * 128 * 2 + n * 8 + n * 8 <= full16 < full32   # bf16 with 64-slot chunks: compact rounds
+    # bf16 with other chunk lengths keeps float32 rounds
+    assert lib.reformer_lsh_workspace_bytes(1, 1, 8, 65536, 128, 4, 1024, 32) >= n * 128 * 4
+    assert lib.reformer_lsh_workspace_bytes(1, 1, 8, 65536, 96, 4, 1024, 64) == 0   # invalid -> 0
+    assert lib.reformer_lsh_workspace_bytes(5, 1, 8, 65536, 128, 4, 1024, 64) == 0  # bad dtype -> 0
     assert lib.reformer_lsh_hash_workspace_bytes(1, 1, 1024, 64, 1, 1) == 0       # one bucket: no scratch
     assert lib.reformer_lsh_sort_workspace_bytes(2, 4, 4096, 2, 64) > 0
-    assert lib.reformer_lsh_attend_workspace_bytes(2, 4, 4096, 64, 2) >= 2 * 4 * 4096 * 2 * 65 * 4
+    assert lib.reformer_lsh_attend_workspace_bytes(0, 2, 4, 4096, 64, 2, 64) >= 2 * 4 * 4096 * 2 * 65 * 4
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

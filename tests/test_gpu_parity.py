@@ -228,3 +228,58 @@ def test_stage_pipeline_equals_fused_entry(nat):
     staged = host(nat.attend(qk, v, perm, w.chunk_len, w.causal))
     fused = host(nat.attention(qk, v, rot, w.n_buckets, w.chunk_len, w.causal))
     np.testing.assert_array_equal(staged, fused)
+
+
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 3e5, 1e30])
+def test_compact_round_storage_keeps_range(nat, scale):
+    """bf16 pipeline stores per-round results compactly (float16 with a per-row
+    power-of-two scale): outputs must track the oracle for tiny and huge values."""
+    import torch
+
+    inp = W.custom_inputs(1, 2, 1024, 64, 32, 2, dtype="bf16", seed=91)
+    vb = W.f32_to_bf16_bits((inp.v * scale).astype(np.float32))
+    v_exact = W.bf16_bits_to_f32(vb)
+    qk, _, rot = to_device(inp)
+    v = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).cuda()
+    out = host(nat.attention(qk, v, rot, 32, 64, True))
+    gb = host(nat.lsh_hash(qk, rot, 32))
+    vmax = float(np.abs(v_exact).max())
+    for h in range(2):
+        want = oracle.lsh_attention_head(inp.qk[0, h].astype(np.float64), v_exact[0, h].astype(np.float64),
+                                         inp.rotations, 32, 64, True, buckets=gb[0, h])["out"]
+        assert np.isfinite(out[0, h]).all()
+        np.testing.assert_allclose(out[0, h], want, rtol=0, atol=2e-2 * vmax / 4)
+
+
+def test_timed_pipeline_matches_and_reports_spans(nat):
+    """reformer_lsh_attention_timed does the same work and records its events in order."""
+    import ctypes
+
+    import torch
+
+    inp = W.make_inputs("small_4k_bf16")
+    w = inp.workload
+    qk, v, rot = to_device(inp)
+    ref = host(nat.attention(qk, v, rot, w.n_buckets, w.chunk_len, w.causal))
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(nat.TIMED_EVENTS)]
+    for ev in events:
+        ev.record()
+    torch.cuda.synchronize()
+    B, H, L, d = qk.shape
+    nbytes = nat.workspace_bytes(B, H, L, d, w.n_rounds, w.n_buckets, w.chunk_len, qk.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(v)
+    arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+    st = nat.lib().reformer_lsh_attention_timed(qk.data_ptr(), v.data_ptr(), rot.data_ptr(), 1, B, H, L, d,
+                                                w.n_rounds, w.n_buckets, w.chunk_len, int(w.causal), out.data_ptr(),
+                                                ws.data_ptr(), nbytes, arr, len(events),
+                                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), ref)
+    spans = [events[i].elapsed_time(events[i + 1]) for i in range(len(events) - 1)]
+    assert all(t >= 0 for t in spans) and sum(spans) > 0
+    bad = nat.lib().reformer_lsh_attention_timed(qk.data_ptr(), v.data_ptr(), rot.data_ptr(), 1, B, H, L, d,
+                                                 w.n_rounds, w.n_buckets, w.chunk_len, int(w.causal), out.data_ptr(),
+                                                 ws.data_ptr(), nbytes, arr, 3, None)
+    assert bad == 1
