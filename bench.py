@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="text_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the oracle runs for cpu_baseline")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the workload the oracle runs for cpu_baseline")
     ap.add_argument("--quiet", action="store_true", help="only print the JSON line")
     ap.add_argument("--profile-stage", choices=["full", "hash", "sort", "attend", "combine", "copy"],
                     help="profiling mode: run the prerequisite stages once, then only this stage --steps times "
