@@ -220,13 +220,13 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(const void* __restric
       tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
       const float m_new = fmaxf(m_run, tmax);
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = exp2f(m_run - m_use);     // 0 when m_run = -inf
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);     // 0 when m_run = -inf
       float psum = 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = exp2f(sc[t][j] - m_use);   // exp2(-inf) = 0 for masked keys
+          const float p = __builtin_amdgcn_exp2f(sc[t][j] - m_use);   // exp2(-inf) = 0 for masked keys
           sc[t][j] = p;
           psum += p;
         }
@@ -416,30 +416,44 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
     }
     sc[t] = acc;
   }
-  float tmax = -INFINITY;
+  // Masks on the raw scores (the scale is applied inside the exponent):
+  // no previous chunk -> its subtiles are empty; the query's own key (row
+  // qrow) sits in subtile 4 + wave at element q16 - 4g; causal -> key
+  // position must precede the query position.
+  if (!has_prev) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int* kp = t < 4 ? ppos : cpos;
-    const u32x4 kp4 = *reinterpret_cast<const u32x4*>(kp + 16 * (t & 3) + 4 * g);   // positions of this lane's 4 keys
+    for (int t = 0; t < 4; ++t) sc[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+  const int jd = q16 - 4 * g;   // diagonal element index when 0 <= jd < 4
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kr = 16 * (t & 3) + 4 * g + j;
-      bool ok = t < 4 ? has_prev : (kr != qrow);
-      if (causal) ok = ok && (static_cast<int>(kp4[j]) < qpos);
-      const float val = ok ? sc[t][j] * scale_log2 : -INFINITY;
-      sc[t][j] = val;
-      tmax = fmaxf(tmax, val);
+  for (int t = 4; t < 8; ++t)
+    if (t - 4 == wave) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == jd) sc[t][j] = -INFINITY;
+    }
+  if (causal) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int* kp = t < 4 ? ppos : cpos;
+      const u32x4 kp4 = *reinterpret_cast<const u32x4*>(kp + 16 * (t & 3) + 4 * g);   // positions of this lane's 4 keys
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[t][j] = static_cast<int>(kp4[j]) < qpos ? sc[t][j] : -INFINITY;
     }
   }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) tmax = fmaxf(tmax, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
   tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
   tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-  const float m_use = (tmax == -INFINITY) ? 0.0f : tmax;
+  // p = 2^((s - max) * scale); a row with no valid key keeps every p = 0.
+  const float m_off = (tmax == -INFINITY) ? 0.0f : -tmax * scale_log2;
   float psum = 0.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float p = exp2f(sc[t][j] - m_use);
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, m_off));
       sc[t][j] = p;
       psum += p;
     }
@@ -481,7 +495,7 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
   const bool empty = (tmax == -INFINITY) || !(lsum > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / lsum;
   const size_t orow = orow_base + qpos;
-  const float zval = empty ? -INFINITY : (tmax + log2f(lsum)) * 0.69314718055994531f;
+  const float zval = empty ? -INFINITY : (tmax * scale_log2 + log2f(lsum)) * 0.69314718055994531f;
   if constexpr (!O16) {
     float* op = out.o + orow * D;
 #pragma unroll
@@ -498,9 +512,10 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(oacc[dt][j] * inv));
+      for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(oacc[dt][j]));
     amax = fmaxf(amax, shfl_xor_f(amax, 16));
     amax = fmaxf(amax, shfl_xor_f(amax, 32));
+    amax *= inv;
     // k = 0 for rows inside the float16 range, else the smallest k with
     // amax * 2^-k < 2^15 (exponent arithmetic on the float bits).
     const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127;

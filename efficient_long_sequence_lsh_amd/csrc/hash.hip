@@ -106,47 +106,69 @@ __global__ void hash_init_kernel(uint32_t* cmax_bits, int n_rounds, int32_t* n_n
   if (threadIdx.x == 0 && n_near_ties != nullptr) *n_near_ties = 0;
 }
 
-// Split-bf16 fragments of R in MFMA A-operand order, plus max column norms.
-// Fragment (round r, tile t, k-step ks, term, lane l) holds, for column
-// c = 32t + l%32 and k0 = 16ks + 8(l/32), the 8 values R[r][k0 + e][c]
-// (zero for c >= half) as bf16 hi (term 0) or lo = bf16(R - hi) (term 1).
-template <int D>
+// Per-call set-up, one workgroup per (tile of 32 rotation columns, round):
+//  - (FRAG) split-bf16 fragments of R in MFMA A-operand order: fragment
+//    (round r, tile t, k-step ks, term, lane l) holds, for column
+//    c = 32t + l%32 and k0 = 16ks + 8(l/32), the 8 values R[r][k0 + e][c]
+//    (zero for c >= half) as bf16 hi (term 0) or lo = bf16(R - hi) (term 1);
+//  - R transposed to float32 [round][column][k], so that the fix-up reads a
+//    column as one contiguous row;
+//  - column norms (float64 sums, rounded up) folded into a per-round max.
+template <int D, bool FRAG>
 __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_ctiles,
-                                                           uint16_t* __restrict__ frag, uint32_t* __restrict__ cmax_bits) {
+                                                           u32x4* __restrict__ frag, float* __restrict__ rt,
+                                                           uint32_t* __restrict__ cmax_bits) {
   constexpr int kSteps = D / 16;
+  constexpr int kGroups = 8;               // k-ranges per column
+  constexpr int kPerG = D / kGroups;       // 8 or 16 values
+  __shared__ double part[kGroups][32];
   const int t = blockIdx.x, r = blockIdx.y;
   const float* R = rot + static_cast<size_t>(r) * D * half;
-  for (int u = threadIdx.x; u < kSteps * 64; u += blockDim.x) {
-    int ks = u / 64, l = u % 64;
-    int c = 32 * t + (l & 31);
-    int k0 = 16 * ks + 8 * (l >> 5);
-    uint16_t hi[8], lo[8];
+  if (FRAG) {
+    for (int u = threadIdx.x; u < kSteps * 64; u += blockDim.x) {
+      const int ks = u / 64, l = u % 64;
+      const int c = 32 * t + (l & 31);
+      const int k0 = 16 * ks + 8 * (l >> 5);
+      u32x4 hi, lo;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float val = (c < half) ? R[static_cast<size_t>(k0 + e) * half + c] : 0.0f;
-      uint16_t h = f32_to_bf16_rne(val);
-      hi[e] = h;
-      lo[e] = f32_to_bf16_rne(val - bf16_to_f32(h));
-    }
-    size_t base = ((((static_cast<size_t>(r) * n_ctiles + t) * kSteps + ks) * 2) * 64 + l) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      frag[base + e] = hi[e];
-      frag[base + 64 * 8 + e] = lo[e];
+      for (int e = 0; e < 8; e += 2) {
+        float v0 = 0.0f, v1 = 0.0f;
+        if (c < half) {
+          v0 = R[static_cast<size_t>(k0 + e) * half + c];
+          v1 = R[static_cast<size_t>(k0 + e + 1) * half + c];
+        }
+        const uint16_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
+        const uint16_t l0 = f32_to_bf16_rne(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16_rne(v1 - bf16_to_f32(h1));
+        hi[e / 2] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lo[e / 2] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+      }
+      const size_t base = (((static_cast<size_t>(r) * n_ctiles + t) * kSteps + ks) * 2) * 64 + l;
+      frag[base] = hi;
+      frag[base + 64] = lo;
     }
   }
-  // Column norms of this tile -> running max per round (non-negative float
-  // bits order like unsigned integers).
+  const int cl = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int c = 32 * t + cl;
+  double acc = 0.0;
+  if (c < half) {
+    float v[kPerG];
+#pragma unroll
+    for (int i = 0; i < kPerG; ++i) {
+      v[i] = R[static_cast<size_t>(g * kPerG + i) * half + c];
+      acc += static_cast<double>(v[i]) * static_cast<double>(v[i]);
+    }
+    f32x4* dst = reinterpret_cast<f32x4*>(rt + (static_cast<size_t>(r) * half + c) * D + g * kPerG);
+#pragma unroll
+    for (int i = 0; i < kPerG / 4; ++i) dst[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+  }
+  part[g][cl] = acc;
+  __syncthreads();
   if (threadIdx.x < 32) {
-    int c = 32 * t + threadIdx.x;
-    double s = 0.0;
-    if (c < half)
-      for (int k = 0; k < D; ++k) {
-        double w = R[static_cast<size_t>(k) * half + c];
-        s += w * w;
-      }
-    float nrm = static_cast<float>(sqrt(s)) * 1.0000005f;   // round up slightly
-    uint32_t bits = __float_as_uint(nrm);
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) sum += part[i][threadIdx.x];
+    uint32_t bits = 0u;
+    if (c < half) bits = __float_as_uint(static_cast<float>(sqrt(sum)) * 1.0000005f);   // round up slightly
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) bits = max(bits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), off, 32)));
     if (threadIdx.x == 0) atomicMax(cmax_bits + r, bits);
@@ -337,92 +359,93 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
   if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
 }
 
-// Column norms only (the float32 path does not need fragments).
-template <int D>
-__global__ void hash_colnorm_kernel(const float* __restrict__ rot, int half, uint32_t* __restrict__ cmax_bits) {
-  const int r = blockIdx.y;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  const float* R = rot + static_cast<size_t>(r) * D * half;
-  uint32_t bits = 0u;
-  if (c < half) {
-    double acc = 0.0;
-    for (int k = 0; k < D; ++k) {
-      double w = R[static_cast<size_t>(k) * half + c];
-      acc += w * w;
-    }
-    bits = __float_as_uint(static_cast<float>(sqrt(acc)) * 1.0000005f);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) bits = max(bits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), off, 64)));
-  if ((threadIdx.x & 63) == 0) atomicMax(cmax_bits + r, bits);
-}
-
 // ---------------------------------------------------------- fix-up ----
-// Re-decide queued (token, round) pairs in float64.  One wavefront per entry.
+// Re-decide queued (token, round) pairs in float64 (products of a bf16 or
+// float32 feature and a float32 rotation entry are exact in float64).  A group
+// of 16 lanes takes one entry: for a pair, lane i holds features
+// [i*D/16, (i+1)*D/16) and the two column dot products are summed across the
+// group; for a full rescore, lane i scores columns i, i+16, ...
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rot,
+__global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
                                                          HashShape s, int32_t* __restrict__ buckets,
                                                          const int32_t* __restrict__ counts, int n_regions, int cap,
                                                          const int32_t* __restrict__ entries_all, int32_t* n_near_ties) {
-  const int lane = threadIdx.x & 63;
-  const int waves = blockDim.x >> 6;
+  constexpr int kPer = D / 16;
+  constexpr int kGroups = 256 / 16;
+  const int sub = threadIdx.x & 15;
+  const int group = threadIdx.x >> 4;
   int seen = 0;
   for (int region = blockIdx.x; region < n_regions; region += gridDim.x) {
-  const int count = counts[region];
-  seen += count;
-  const int32_t* entries = entries_all + 3 * static_cast<size_t>(region) * cap;
-  for (int e = threadIdx.x >> 6; e < count; e += waves) {
-    const int tok = entries[3 * static_cast<size_t>(e)];
-    const int w1 = entries[3 * static_cast<size_t>(e) + 1];
-    const int w2 = entries[3 * static_cast<size_t>(e) + 2];
-    const int round = w1 & 0x7fffffff;
-    const bool full = (w1 & static_cast<int>(0x80000000u)) != 0;
-    const float* R = rot + static_cast<size_t>(round) * D * s.half;
-    auto xval = [&](int k) -> double {
-      if (BF16) return static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[static_cast<size_t>(tok) * D + k]));
-      return static_cast<double>(static_cast<const float*>(qk_raw)[static_cast<size_t>(tok) * D + k]);
-    };
-    // Best candidate as (value, bucket): larger value wins, equal values go to the lower bucket.
-    double best_v = -1.0;
-    int best_b = 0x7fffffff;
-    auto offer = [&](double p, int c) {
-      double v = p >= 0.0 ? p : -p;
-      int b = p >= 0.0 ? c : c + s.half;   // p == 0: +p (lower bucket) and -p tie; lower wins
-      if (v > best_v || (v == best_v && b < best_b)) { best_v = v; best_b = b; }
-    };
-    if (!full) {
-      const int c1 = w2 & 0xffff, c2 = (w2 >> 16) & 0xffff;
-      double p1 = 0.0, p2 = 0.0;
-      for (int k = lane; k < D; k += 64) {
-        double xv = xval(k);
-        if (c1 < s.half) p1 += xv * static_cast<double>(R[static_cast<size_t>(k) * s.half + c1]);
-        if (c2 < s.half) p2 += xv * static_cast<double>(R[static_cast<size_t>(k) * s.half + c2]);
-      }
+    const int count = counts[region];
+    seen += count;
+    const int32_t* entries = entries_all + 3 * static_cast<size_t>(region) * cap;
+    for (int e = group; e < count; e += kGroups) {
+      const int tok = entries[3 * static_cast<size_t>(e)];
+      const int w1 = entries[3 * static_cast<size_t>(e) + 1];
+      const int w2 = entries[3 * static_cast<size_t>(e) + 2];
+      const int round = w1 & 0x7fffffff;
+      const bool full = (w1 & static_cast<int>(0x80000000u)) != 0;
+      const float* R = rt + static_cast<size_t>(round) * s.half * D;
+      auto xval = [&](int k) -> double {
+        if (BF16) return static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[static_cast<size_t>(tok) * D + k]));
+        return static_cast<double>(static_cast<const float*>(qk_raw)[static_cast<size_t>(tok) * D + k]);
+      };
+      // Best candidate as (value, bucket): larger value wins, equal values go to the lower bucket.
+      double best_v = -1.0;
+      int best_b = 0x7fffffff;
+      auto offer = [&](double p, int c) {
+        double v = p >= 0.0 ? p : -p;
+        int b = p >= 0.0 ? c : c + s.half;   // p == 0: +p (lower bucket) and -p tie; lower wins
+        if (v > best_v || (v == best_v && b < best_b)) { best_v = v; best_b = b; }
+      };
+      if (!full) {
+        const int c1 = w2 & 0xffff, c2 = (w2 >> 16) & 0xffff;
+        double xv[kPer];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        p1 += shfl_xor_d(p1, off);
-        p2 += shfl_xor_d(p2, off);
-      }
-      if (c1 < s.half) offer(p1, c1);
-      if (c2 < s.half && c2 != c1) offer(p2, c2);
-    } else {
-      for (int c = lane; c < s.half; c += 64) {
-        double p = 0.0;
-        for (int k = 0; k < D; ++k) p += xval(k) * static_cast<double>(R[static_cast<size_t>(k) * s.half + c]);
-        offer(p, c);
-      }
+        for (int i = 0; i < kPer; ++i) xv[i] = xval(sub * kPer + i);
+        double p1 = 0.0, p2 = 0.0;
+        const f32x4* r1 = reinterpret_cast<const f32x4*>(R + static_cast<size_t>(min(c1, s.half - 1)) * D + sub * kPer);
+        const f32x4* r2 = reinterpret_cast<const f32x4*>(R + static_cast<size_t>(min(c2, s.half - 1)) * D + sub * kPer);
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        double ov = shfl_xor_d(best_v, off);
-        int ob = __shfl_xor(best_b, off, 64);
-        if (ov > best_v || (ov == best_v && ob < best_b)) { best_v = ov; best_b = ob; }
+        for (int i = 0; i < kPer / 4; ++i) {
+          const f32x4 a = r1[i], b = r2[i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p1 += xv[4 * i + j] * static_cast<double>(a[j]);
+            p2 += xv[4 * i + j] * static_cast<double>(b[j]);
+          }
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+          p1 += shfl_xor_d(p1, off);
+          p2 += shfl_xor_d(p2, off);
+        }
+        if (c1 < s.half) offer(p1, c1);
+        if (c2 < s.half && c2 != c1) offer(p2, c2);
+      } else {
+        for (int c = sub; c < s.half; c += 16) {
+          const f32x4* rc = reinterpret_cast<const f32x4*>(R + static_cast<size_t>(c) * D);
+          double p = 0.0;
+#pragma unroll 2
+          for (int i = 0; i < D / 4; ++i) {
+            const f32x4 a = rc[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p += xval(4 * i + j) * static_cast<double>(a[j]);
+          }
+          offer(p, c);
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+          double ov = shfl_xor_d(best_v, off);
+          int ob = __shfl_xor(best_b, off, 64);
+          if (ov > best_v || (ov == best_v && ob < best_b)) { best_v = ov; best_b = ob; }
+        }
+      }
+      if (sub == 0) {
+        int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
+        buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = best_b;
       }
     }
-    if (lane == 0) {
-      int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
-      buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = best_b;
-    }
-  }
   }
   if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
 }
@@ -458,11 +481,12 @@ HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds
 HashScratch hash_scratch(const HashShape& s) {
   HashScratch h{};
   h.frag_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * 32 * s.d * 2 * sizeof(uint16_t), 256);
+  h.rt_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.half * s.d * sizeof(float), 256);
   h.cmax_bytes = align_up(static_cast<size_t>(s.n_rounds) * sizeof(uint32_t), 256);
   const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
   h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
   h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
-  h.total = h.frag_bytes + h.cmax_bytes + h.counter_bytes + h.list_bytes;
+  h.total = h.frag_bytes + h.rt_bytes + h.cmax_bytes + h.counter_bytes + h.list_bytes;
   return h;
 }
 
@@ -477,39 +501,41 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
                        int32_t* n_near_ties, void* workspace, hipStream_t stream, hipEvent_t* marks) {
   HashScratch h = hash_scratch(s);
   char* ws = static_cast<char*>(workspace);
-  uint16_t* frag = reinterpret_cast<uint16_t*>(ws);
-  uint32_t* cmax = reinterpret_cast<uint32_t*>(ws + h.frag_bytes);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + h.frag_bytes + h.cmax_bytes);
-  int32_t* list = reinterpret_cast<int32_t*>(ws + h.frag_bytes + h.cmax_bytes + h.counter_bytes);
+  u32x4* frag = reinterpret_cast<u32x4*>(ws);
+  ws += h.frag_bytes;
+  float* rt = reinterpret_cast<float*>(ws);
+  ws += h.rt_bytes;
+  uint32_t* cmax = reinterpret_cast<uint32_t*>(ws);
+  ws += h.cmax_bytes;
+  int32_t* counts = reinterpret_cast<int32_t*>(ws);
+  ws += h.counter_bytes;
+  int32_t* list = reinterpret_cast<int32_t*>(ws);
   const int n_regions = (s.n_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
   const int cap = kTokensPerBlock * s.n_rounds;
   NearTieList lst{counts, list, cap, nullptr};
 
   hipLaunchKernelGGL(hash_init_kernel, dim3(1), dim3(256), 0, stream, cmax, s.n_rounds, n_near_ties);
+  const dim3 pg(s.n_ctiles, s.n_rounds);
+  const dim3 grid(n_regions);
   if (bf16) {
-    dim3 pg(s.n_ctiles, s.n_rounds);
-    dim3 grid(n_regions);
     const uint16_t* x = static_cast<const uint16_t*>(qk);
-    const u32x4* fv = reinterpret_cast<const u32x4*>(frag);
     if (s.d == 64) {
-      hipLaunchKernelGGL(hash_prepare_kernel<64>, pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, fv, cmax, s, buckets, lst);
+      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, cmax, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL(hash_prepare_kernel<128>, pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, fv, cmax, s, buckets, lst);
+      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, cmax, s, buckets, lst);
     }
   } else {
-    dim3 ng((s.half + 255) / 256, s.n_rounds);
-    dim3 grid(n_regions);
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL(hash_colnorm_kernel<64>, ng, dim3(256), 0, stream, rotations, s.half, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL(hash_colnorm_kernel<128>, ng, dim3(256), 0, stream, rotations, s.half, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
     }
@@ -518,14 +544,14 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   const int fix_blocks = std::min(n_regions, 2048);
   if (s.d == 64) {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
   }
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();

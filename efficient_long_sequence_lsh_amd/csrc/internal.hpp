@@ -24,6 +24,7 @@ HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds
 // Byte sizes of the hash scratch regions, in workspace order.
 struct HashScratch {
   size_t frag_bytes;     // split-bf16 rotation fragments
+  size_t rt_bytes;       // rotations transposed to float32 [round][column][k]
   size_t cmax_bytes;     // per-round max column norm (float bits)
   size_t counter_bytes;  // near-tie counter
   size_t list_bytes;     // near-tie list (3 int32 per entry, capacity n_tokens * n_rounds)

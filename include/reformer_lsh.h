@@ -118,8 +118,9 @@ rlsh_status_t reformer_lsh_hash(const void* qk, rlsh_dtype_t dtype, const float*
  * Stable sort of each (batch, head, round) segment by bucket id; ties keep
  * position order (Summary: "sorted by bucket").
  *
- * buckets   int32 [B, H, n_rounds, L], values in [0, n_buckets) (values
- *           outside that range are undefined behaviour).
+ * buckets   int32 [B, H, n_rounds, L], values in [0, n_buckets); a value
+ *           outside that range is clamped into it (sorted as 0 or
+ *           n_buckets - 1), so the output is always a permutation.
  * perm      int32 [B, H, n_rounds, L], written: perm[.., s] = original
  *           position at sorted slot s.
  * inv_perm  int32 [B, H, n_rounds, L], written: inv_perm[.., perm[.., s]] = s.

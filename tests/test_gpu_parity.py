@@ -95,6 +95,7 @@ def test_hash_one_bucket(nat):
     (1, 1, 1, 33000, 16384, True),
     (1, 1, 1, 5, 2, False),
     (2, 1, 1, 3000, 1, False),           # one bucket: identity
+    (8, 8, 8, 1200, 192, True),          # many segments (block count not a multiple of 8)
 ])
 def test_sort(nat, B, H, r, L, nb, skew):
     import torch
@@ -110,6 +111,18 @@ def test_sort(nat, B, H, r, L, nb, skew):
     keys = keys.astype(np.int32)
     perm, inv = nat.lsh_sort(torch.from_numpy(keys).cuda(), nb)
     want_p, want_i = oracle_perm(keys)
+    np.testing.assert_array_equal(host(perm), want_p)
+    np.testing.assert_array_equal(host(inv), want_i)
+
+
+def test_sort_clamps_out_of_range_keys(nat):
+    """Keys below 0 sort as 0 and keys >= n_buckets as n_buckets - 1."""
+    import torch
+
+    g = np.random.default_rng(7)
+    keys = g.integers(-40, 80, size=(1, 2, 2, 3001)).astype(np.int32)
+    perm, inv = nat.lsh_sort(torch.from_numpy(keys).cuda(), 64)
+    want_p, want_i = oracle_perm(np.clip(keys, 0, 63))
     np.testing.assert_array_equal(host(perm), want_p)
     np.testing.assert_array_equal(host(inv), want_i)
 
@@ -170,6 +183,32 @@ def test_combine(nat, dtype):
             tol = 1e-5 if dtype == "f32" else 2 ** -8 * np.abs(want).max()
             np.testing.assert_allclose(out[b, h], want, rtol=0, atol=tol)
             np.testing.assert_array_equal(out[b, h, :7], inp.v[b, h, :7])
+
+
+def test_combine_bf16_output_rounds_to_nearest_even(nat):
+    """One round with z = 0 passes o through unchanged (weight 1, sum 1), so
+    the bf16 output is exactly the round-to-nearest-even image of o: ties,
+    subnormals, zero, large and infinite values.  (-0 is left out: the
+    weighted sum starts from +0, so -0 * 1 + 0 = +0 by IEEE rules.)"""
+    import torch
+
+    g = np.random.default_rng(23)
+    L, d = 256, 64
+    base = W.bf16_bits_to_f32(g.integers(0, 1 << 16, size=(L, d)).astype(np.uint16))
+    base[~np.isfinite(base)] = 1.0
+    half_ulp = np.abs(base) * np.float32(2.0 ** -8)
+    vals = [g.standard_normal((L, d)).astype(np.float32),
+            (base + half_ulp).astype(np.float32),                      # near and at ties
+            (g.standard_normal((L, d)) * 1e-39).astype(np.float32),    # float32 subnormals
+            np.clip(g.standard_normal((L, d)) * 3e38, -3.4e38, 3.4e38).astype(np.float32)]
+    o = np.concatenate(vals, axis=0)
+    o[0, :3] = [0.0, np.inf, -np.inf]
+    n = o.shape[0]
+    z = np.zeros((1, 1, 1, n), dtype=np.float32)
+    v = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device="cuda")
+    out = nat.combine(torch.from_numpy(o.reshape(1, 1, 1, n, d)).cuda(), torch.from_numpy(z).cuda(), v)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(n, d)
+    np.testing.assert_array_equal(got, W.f32_to_bf16_bits(o))
 
 
 # ------------------------------------------------------------ end to end ----
