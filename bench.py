@@ -164,30 +164,45 @@ def stage_work(w):
     Per head-token (N = batch * heads * seq_len) and round r: the hash projects
     onto b/2 rotation columns (2 d b/2 flops); chunk attention gathers one qk and
     one v row plus the permutation entry and writes one o row plus its
-    normaliser; the combine reads the r rows and writes the output row.
+    normaliser; the combine reads the r rows and writes the output row.  In the
+    compact bf16 pipeline the last round's attention launch does the combine
+    itself: "attend" then covers rounds 0..r-2 and "combine" the last round
+    (gather, no o written) plus the reads of the earlier rounds and the output.
     """
     N = w.batch * w.heads * w.seq_len
     r, d, b = w.n_rounds, w.d_head, w.n_buckets
     e = 2 if w.dtype == "bf16" else 4
-    o_row, z_row = (2 * d, 8) if compact_rounds(w) else (4 * d, 4)
+    window = min(2 * w.chunk_len, w.seq_len)
+    gather = 2 * d * e + 4
+    if compact_rounds(w):
+        o_row = 2 * d + 8
+        attend = {"bytes": N * (r - 1) * (gather + o_row), "flops": N * (r - 1) * 4 * window * d}
+        combine = {"bytes": N * (gather + (r - 1) * o_row + d * e), "flops": N * 4 * window * d}
+    else:
+        o_row = 4 * d + 4
+        attend = {"bytes": N * r * (gather + o_row), "flops": N * r * 4 * window * d}
+        combine = {"bytes": N * (r * o_row + d * e)}
     return {
         "hash": {"flops": N * r * d * b, "bytes": N * (d * e + 4 * r)},
         "sort": {"bytes": N * r * 12},   # bucket ids read by histogram and scatter, perm written
-        "attend": {"bytes": N * r * (2 * d * e + 4 + o_row + z_row),
-                   "flops": N * r * 4 * min(2 * w.chunk_len, w.seq_len) * d},
-        "combine": {"bytes": N * (r * (o_row + z_row) + d * e)},
+        "attend": attend,
+        "combine": combine,
     }
 
 
 def kernel_of_stage(w):
-    attend = "chunk_attend64_kernel" if w.dtype == "bf16" and min(w.chunk_len, w.seq_len) == 64 else "chunk_attend_kernel"
-    combine = "combine_compact_kernel" if compact_rounds(w) else "combine_kernel"
+    fast = w.dtype == "bf16" and min(w.chunk_len, w.seq_len) == 64
+    if compact_rounds(w):
+        attend, combine = "chunk_attend64_kernel<compact>", "chunk_attend64_kernel<final>"
+    else:
+        attend, combine = ("chunk_attend64_kernel" if fast else "chunk_attend_kernel"), "combine_kernel"
     hash_k = "hash_mfma_kernel" if w.dtype == "bf16" else "hash_fma_kernel"
     return {
         "hash": (hash_k, "efficient_long_sequence_lsh_amd/csrc/hash.hip"),
-        "sort": ("sort_hist_kernel+sort_scan*+sort_scatter_kernel", "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
+        "sort": ("sort_hist_kernel+sort_scan_kernel+sort_scatter_kernel", "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
         "attend": (attend, "efficient_long_sequence_lsh_amd/csrc/attend.hip"),
-        "combine": (combine, "efficient_long_sequence_lsh_amd/csrc/combine.hip"),
+        "combine": (combine, "efficient_long_sequence_lsh_amd/csrc/attend.hip" if compact_rounds(w)
+                    else "efficient_long_sequence_lsh_amd/csrc/combine.hip"),
     }
 
 

@@ -146,9 +146,8 @@ hipError_t run_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const i
   if (rl.compact) {
     uint16_t* o16 = static_cast<uint16_t*>(o_mem);
     float2* zk = static_cast<float2*>(z_mem);
-    e = rlsh::launch_chunk_attend_compact(qk, v, perm, bh, seq_len, d_head, n_rounds, causal != 0, o16, zk, stream);
-    if (e == hipSuccess && mark) e = hipEventRecord(*mark, stream);
-    if (e == hipSuccess) e = rlsh::launch_combine_compact(o16, zk, v, bh, seq_len, d_head, n_rounds, out, stream);
+    e = rlsh::launch_attend_combine_compact(qk, v, perm, bh, seq_len, d_head, n_rounds, causal != 0, o16, zk, out,
+                                            stream, mark);
   } else {
     float* o = static_cast<float*>(o_mem);
     float* z = static_cast<float*>(z_mem);

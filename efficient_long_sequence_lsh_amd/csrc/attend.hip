@@ -369,24 +369,39 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& t, Lds64<D>& sh, i
   }
 }
 
-// Where a round's per-position results go.  Plain: o float32 [.., d] and z
-// float32.  Compact (bf16 inputs inside the pipeline): o as float16 scaled by
-// 2^-k per row (k = 0 unless the row's largest magnitude reaches 2^15) and
-// (z, k) as a float pair; this halves the bytes of the largest intermediate
-// while keeping 11 significant bits.
+// Where a round's per-position results go.
+//  kSinkF32:     o float32 [.., d] and z float32 (the stage entry point).
+//  kSinkCompact: o as float16 scaled by 2^-k per row (k = 0 unless the row's
+//                largest magnitude reaches 2^15) and (z, k) as a float pair;
+//                half the bytes of float32 while keeping 11 significant bits.
+//  kSinkFinal:   the last round of the bf16 pipeline combines in place: it
+//                reads the compact results of the earlier rounds at the
+//                query's position, applies the logsumexp weights (self
+//                fallback when no round has a target) and writes the bf16
+//                output row, so its own o is never stored.
+//  kSinkFinal + 1 + np: the same with the np earlier rounds' rows loaded at
+//                the start of each chunk, so their latency hides behind the
+//                chunk's own work (np = r - 1 for the common round counts).
+constexpr int kSinkF32 = 0;
+constexpr int kSinkCompact = 1;
+constexpr int kSinkFinal = 2;
+constexpr int sink_final_prefetch(int np) { return kSinkFinal + 1 + np; }
+
 struct RoundSink {
-  float* o;          // plain
-  float* z;          // plain
-  uint16_t* o16;     // compact
-  float2* zk;        // compact
+  float* o;              // kSinkF32
+  float* z;              // kSinkF32
+  uint16_t* o16;         // kSinkCompact: this launch's rounds; kSinkFinal: earlier rounds (read)
+  float2* zk;            // as o16
+  const uint16_t* v;     // kSinkFinal: self fallback rows
+  uint16_t* out;         // kSinkFinal: output [bh, L, d]
 };
 
 // One chunk: queries = rows of buffer `cur`, keys = rows of `prv` (previous
 // chunk, if any) and `cur`.  Writes o and z by original position.
-template <int D, bool O16>
+template <int D, int MODE>
 __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int prv, bool has_prev, const int* cpos,
                                                const int* ppos, int causal, float scale_log2, size_t orow_base,
-                                               RoundSink out) {
+                                               size_t row0, int seq_len, int n_prev, RoundSink out) {
   constexpr int kKP = Lds64<D>::kKPitch;
   constexpr int kVP = Lds64<D>::kVPitch;
   const int lane = threadIdx.x & 63;
@@ -395,6 +410,24 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
   const int g = lane >> 4;
   const int qrow = 16 * wave + q16;          // query row inside the chunk
   const int qpos = cpos[qrow];
+  // Final-round sink with a compile-time round count: earlier rounds' (z, k)
+  // and this lane's features of their o rows, loaded now.
+  constexpr bool kPre = MODE > kSinkFinal;
+  constexpr int kNP = kPre ? MODE - kSinkFinal - 1 : 0;
+  constexpr int kNPA = kNP > 0 ? kNP : 1;
+  float2 zpre[kNPA];
+  u32x2 opre[kNPA][D / 16];
+  if constexpr (kPre) {
+    const size_t prow0 = row0 * (kNP + 1) + qpos;
+#pragma unroll
+    for (int rho = 0; rho < kNP; ++rho) {
+      const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
+      zpre[rho] = out.zk[pr];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        opre[rho][dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
+    }
+  }
   bf16x8 qf[D / 32];
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
@@ -496,7 +529,7 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
   const float inv = empty ? 0.0f : 1.0f / lsum;
   const size_t orow = orow_base + qpos;
   const float zval = empty ? -INFINITY : (tmax * scale_log2 + log2f(lsum)) * 0.69314718055994531f;
-  if constexpr (!O16) {
+  if constexpr (MODE == kSinkF32) {
     float* op = out.o + orow * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -506,7 +539,7 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
       *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = r;
     }
     if (g == 0) out.z[orow] = zval;
-  } else {
+  } else if constexpr (MODE == kSinkCompact) {
     // Row maximum (the row is spread over the 4 lanes q16 + 16g).
     float amax = 0.0f;
 #pragma unroll
@@ -536,28 +569,98 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
       *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = pk;
     }
     if (g == 0) out.zk[orow] = make_float2(zval, static_cast<float>(k));
+  } else {
+    // Round combine at this position: rounds 0..n_prev-1 are stored compact
+    // at rows (round0 + rho) * L + qpos; this round's o is still in registers.
+    const int np = kPre ? kNP : n_prev;
+    const size_t prow0 = row0 * (np + 1) + qpos;   // round 0 of this (batch, head)
+    auto zk_of = [&](int rho) -> float2 {
+      if constexpr (kPre) return zpre[rho];
+      return out.zk[prow0 + static_cast<size_t>(rho) * seq_len];
+    };
+    float zmax = zval;
+    if constexpr (kPre) {
+#pragma unroll
+      for (int rho = 0; rho < kNP; ++rho) zmax = fmaxf(zmax, zpre[rho].x);
+    } else {
+      for (int rho = 0; rho < np; ++rho) zmax = fmaxf(zmax, zk_of(rho).x);
+    }
+    u32x2 res[D / 16];
+    if (zmax == -INFINITY) {   // no round has a valid target: the token's own value
+      const uint16_t* vp = out.v + (row0 + qpos) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) res[dt] = *reinterpret_cast<const u32x2*>(vp + 16 * dt + 4 * g);
+    } else {
+      const float w_this = empty ? 0.0f : __expf(zval - zmax);
+      float wsum = w_this;
+      const float c_this = w_this * inv;
+      float acc[D / 16][4];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[dt][j] = oacc[dt][j] * c_this;
+      // Adds round rho's stored row (float16 features times 2^k) with its weight.
+      auto add_round = [&](const float2 e, const u32x2 (&h)[D / 16]) {
+        const float w = __expf(e.x - zmax);   // 0 for rounds without a target
+        wsum += w;
+        const float ws = w * __uint_as_float(static_cast<uint32_t>(127 + static_cast<int>(e.y)) << 23);   // w * 2^k
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h[dt][q] & 0xffffu));
+            const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h[dt][q] >> 16));
+            acc[dt][2 * q] = fmaf(ws, static_cast<float>(lo), acc[dt][2 * q]);
+            acc[dt][2 * q + 1] = fmaf(ws, static_cast<float>(hi), acc[dt][2 * q + 1]);
+          }
+      };
+      if constexpr (kPre) {
+#pragma unroll
+        for (int rho = 0; rho < kNP; ++rho) add_round(zpre[rho], opre[rho]);
+      } else {
+        for (int rho = 0; rho < np; ++rho) {
+          const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
+          const float2 e = out.zk[pr];
+          u32x2 h[D / 16];
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) h[dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
+          add_round(e, h);
+        }
+      }
+      const float rs = 1.0f / wsum;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        res[dt][0] = pack_bf16x2(acc[dt][0] * rs, acc[dt][1] * rs);
+        res[dt][1] = pack_bf16x2(acc[dt][2] * rs, acc[dt][3] * rs);
+      }
+    }
+    uint16_t* dst = out.out + (row0 + qpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<u32x2*>(dst + 16 * dt + 4 * g) = res[dt];
   }
 }
 
-template <int D, bool O16>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* __restrict__ qk,
                                                                 const uint16_t* __restrict__ vv,
                                                                 const int32_t* __restrict__ perm_all, AttnShape s,
-                                                                int n_seg, int runs_per_seg, int per_xcd,
-                                                                RoundSink out) {
+                                                                int n_seg, int launch_rounds, int round_base,
+                                                                int runs_per_seg, int per_xcd, RoundSink out) {
   __shared__ Lds64<D> sh;
   // XCD-aware mapping: hardware places block b on XCD b % 8; give each XCD a
   // contiguous range of runs.
   const int b = blockIdx.x;
   const int logical = (b % 8) * per_xcd + b / 8;
   if (logical >= n_seg * runs_per_seg) return;
-  const int seg = logical / runs_per_seg;
-  const int run = logical - seg * runs_per_seg;
-  const int bh = seg / s.n_rounds;
+  const int lseg = logical / runs_per_seg;
+  const int run = logical - lseg * runs_per_seg;
+  const int bh = lseg / launch_rounds;
+  const int seg = bh * s.n_rounds + round_base + (lseg - bh * launch_rounds);
   const int L = s.seq_len;
   const int32_t* perm = perm_all + static_cast<size_t>(seg) * L;
   const size_t row0 = static_cast<size_t>(bh) * L;
   const size_t orow_base = static_cast<size_t>(seg) * L;
+  const int n_prev = s.n_rounds - 1;   // used by kSinkFinal (the last round)
   const int c_begin = run * kRun64;
   const int c_end = min(s.n_qt, c_begin + kRun64);
 
@@ -588,8 +691,8 @@ __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* 
   while (true) {
     // ra holds chunk c+1 (if any)
     if (c + 2 < c_end) gather_tile<D>(rb, qk, vv, pos_of(c + 2), row0);
-    attend_chunk64<D, O16>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base,
-                           out);
+    attend_chunk64<D, MODE>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base,
+                            row0, L, n_prev, out);
     __syncthreads();
     if (c + 1 < c_end) store_tile<D>(ra, sh, cur ^ 1);
     __syncthreads();
@@ -597,8 +700,8 @@ __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* 
     if (++c >= c_end) break;
     // rb holds chunk c+1 (if any)
     if (c + 2 < c_end) gather_tile<D>(ra, qk, vv, pos_of(c + 2), row0);
-    attend_chunk64<D, O16>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base,
-                           out);
+    attend_chunk64<D, MODE>(sh, cur, cur ^ 1, c > 0, pos_of(c), pos_of(c - 1), s.causal, s.scale_log2, orow_base,
+                            row0, L, n_prev, out);
     __syncthreads();
     if (c + 1 < c_end) store_tile<D>(rb, sh, cur ^ 1);
     __syncthreads();
@@ -607,15 +710,17 @@ __global__ __launch_bounds__(256, 2) void chunk_attend64_kernel(const uint16_t* 
   }
 }
 
-template <int D, bool O16>
-hipError_t launch_fast64(const void* qk, const void* v, const int32_t* perm, int n_seg, AttnShape s, RoundSink out,
-                         hipStream_t stream) {
+template <int D, int MODE>
+hipError_t launch_fast64(const void* qk, const void* v, const int32_t* perm, int bh, int launch_rounds, int round_base,
+                         AttnShape s, RoundSink out, hipStream_t stream) {
   const int runs_per_seg = (s.n_qt + kRun64 - 1) / kRun64;
+  const int n_seg = bh * launch_rounds;
   const int total = n_seg * runs_per_seg;
+  if (total == 0) return hipSuccess;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((chunk_attend64_kernel<D, O16>), dim3(8 * per_xcd), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(v), perm, s, n_seg, runs_per_seg,
-                     per_xcd, out);
+  hipLaunchKernelGGL((chunk_attend64_kernel<D, MODE>), dim3(8 * per_xcd), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(v), perm, s, n_seg, launch_rounds,
+                     round_base, runs_per_seg, per_xcd, out);
   return hipGetLastError();
 }
 
@@ -641,9 +746,9 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   const int n_seg = bh * n_rounds;
   if (bf16 && s.chunk == kKTile && seq_len % kKTile == 0) {
-    RoundSink out{o_rounds, z_rounds, nullptr, nullptr};
-    return d == 64 ? launch_fast64<64, false>(qk, v, perm, n_seg, s, out, stream)
-                   : launch_fast64<128, false>(qk, v, perm, n_seg, s, out, stream);
+    RoundSink out{o_rounds, z_rounds, nullptr, nullptr, nullptr, nullptr};
+    return d == 64 ? launch_fast64<64, kSinkF32>(qk, v, perm, bh, n_rounds, 0, s, out, stream)
+                   : launch_fast64<128, kSinkF32>(qk, v, perm, bh, n_rounds, 0, s, out, stream);
   }
   if (d == 64) {
     return bf16 ? launch_typed<64, true>(qk, v, perm, n_seg, s, o_rounds, z_rounds, stream)
@@ -657,8 +762,16 @@ bool compact_rounds_supported(bool bf16, int seq_len, int chunk_len) {
   return bf16 && std::min(chunk_len, seq_len) == kKTile && seq_len % kKTile == 0;
 }
 
-hipError_t launch_chunk_attend_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len, int d,
-                                       int n_rounds, bool causal, uint16_t* o16, float2* zk, hipStream_t stream) {
+template <int MODE>
+hipError_t launch_final(const void* qk, const void* v, const int32_t* perm, int bh, int d, AttnShape s, RoundSink sink,
+                        hipStream_t stream) {
+  return d == 64 ? launch_fast64<64, MODE>(qk, v, perm, bh, 1, s.n_rounds - 1, s, sink, stream)
+                 : launch_fast64<128, MODE>(qk, v, perm, bh, 1, s.n_rounds - 1, s, sink, stream);
+}
+
+hipError_t launch_attend_combine_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len,
+                                         int d, int n_rounds, bool causal, uint16_t* o16, float2* zk, void* out,
+                                         hipStream_t stream, hipEvent_t* mark) {
   AttnShape s{};
   s.seq_len = seq_len;
   s.chunk = kKTile;
@@ -666,10 +779,20 @@ hipError_t launch_chunk_attend_compact(const void* qk, const void* v, const int3
   s.n_qt = seq_len / kKTile;
   s.causal = causal ? 1 : 0;
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-  RoundSink out{nullptr, nullptr, o16, zk};
-  const int n_seg = bh * n_rounds;
-  return d == 64 ? launch_fast64<64, true>(qk, v, perm, n_seg, s, out, stream)
-                 : launch_fast64<128, true>(qk, v, perm, n_seg, s, out, stream);
+  RoundSink sink{nullptr, nullptr, o16, zk, static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out)};
+  hipError_t e = d == 64 ? launch_fast64<64, kSinkCompact>(qk, v, perm, bh, n_rounds - 1, 0, s, sink, stream)
+                         : launch_fast64<128, kSinkCompact>(qk, v, perm, bh, n_rounds - 1, 0, s, sink, stream);
+  if (e == hipSuccess && mark != nullptr) e = hipEventRecord(*mark, stream);
+  if (e != hipSuccess) return e;
+  switch (n_rounds) {
+    case 1: return launch_final<sink_final_prefetch(0)>(qk, v, perm, bh, d, s, sink, stream);
+    case 2: return launch_final<sink_final_prefetch(1)>(qk, v, perm, bh, d, s, sink, stream);
+    case 4: return launch_final<sink_final_prefetch(3)>(qk, v, perm, bh, d, s, sink, stream);
+    case 8:   // seven prefetched rows fit the register budget at d = 64 only
+      if (d == 64) return launch_fast64<64, sink_final_prefetch(7)>(qk, v, perm, bh, 1, 7, s, sink, stream);
+      return launch_final<kSinkFinal>(qk, v, perm, bh, d, s, sink, stream);
+    default: return launch_final<kSinkFinal>(qk, v, perm, bh, d, s, sink, stream);
+  }
 }
 
 }  // namespace rlsh

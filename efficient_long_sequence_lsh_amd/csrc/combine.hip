@@ -75,56 +75,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-// Compact per-round results (bf16 pipeline): o as float16 scaled by 2^-k,
-// (z, k) pairs.  Each thread owns 8 consecutive features (16-byte loads).
-template <int D>
-__global__ __launch_bounds__(256) void combine_compact_kernel(const uint16_t* __restrict__ o16,
-                                                              const float2* __restrict__ zk,
-                                                              const uint16_t* __restrict__ v, int n_rows,
-                                                              int seq_len, int n_rounds, uint16_t* __restrict__ out) {
-  constexpr int kTpr = D / 8;
-  constexpr int kRowsPerBlock = 256 / kTpr;
-  const int sub = threadIdx.x % kTpr;
-  const int rsub = threadIdx.x / kTpr;
-  for (int row = blockIdx.x * kRowsPerBlock + rsub; row < n_rows; row += gridDim.x * kRowsPerBlock) {
-    const int bh = row / seq_len;
-    const int pos = row - bh * seq_len;
-    const size_t zrow = static_cast<size_t>(bh) * n_rounds * seq_len + pos;   // round 0
-    float zmax = -INFINITY;
-    for (int r = 0; r < n_rounds; ++r) zmax = fmaxf(zmax, zk[zrow + static_cast<size_t>(r) * seq_len].x);
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-    u32x4 packed;
-    if (zmax == -INFINITY) {
-      packed = *reinterpret_cast<const u32x4*>(v + static_cast<size_t>(row) * D + 8 * sub);   // self fallback
-    } else {
-      float wsum = 0.0f;
-      for (int r = 0; r < n_rounds; ++r) {
-        const size_t zi = zrow + static_cast<size_t>(r) * seq_len;
-        const float2 e = zk[zi];
-        const float w = expf(e.x - zmax);   // 0 for rounds without a target
-        wsum += w;
-        if (w > 0.0f) {
-          const float ws = w * __uint_as_float(static_cast<uint32_t>(127 + static_cast<int>(e.y)) << 23);   // w * 2^k
-          const u32x4 h = *reinterpret_cast<const u32x4*>(o16 + zi * D + 8 * sub);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h[q] & 0xffffu));
-            const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h[q] >> 16));
-            acc[2 * q] = fmaf(ws, static_cast<float>(lo), acc[2 * q]);
-            acc[2 * q + 1] = fmaf(ws, static_cast<float>(hi), acc[2 * q + 1]);
-          }
-        }
-      }
-      const float inv = 1.0f / wsum;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) packed[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
-    }
-    *reinterpret_cast<u32x4*>(out + static_cast<size_t>(row) * D + 8 * sub) = packed;
-  }
-}
-
 template <int D, bool BF16>
 hipError_t launch_typed(const float* o, const float* z, const void* v, int n_rows, int seq_len, int n_rounds,
                         void* out, hipStream_t stream) {
@@ -146,20 +96,6 @@ hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const vo
                 : launch_typed<64, false>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream);
   return bf16 ? launch_typed<128, true>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream)
               : launch_typed<128, false>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream);
-}
-
-hipError_t launch_combine_compact(const uint16_t* o16, const float2* zk, const void* v, int bh, int seq_len, int d,
-                                  int n_rounds, void* out, hipStream_t stream) {
-  const int n_rows = bh * seq_len;
-  const int rows_per_block = 256 / (d / 8);
-  int blocks = std::max(1, std::min((n_rows + rows_per_block - 1) / rows_per_block, 256 * 32));
-  if (d == 64)
-    hipLaunchKernelGGL(combine_compact_kernel<64>, dim3(blocks), dim3(256), 0, stream, o16, zk,
-                       static_cast<const uint16_t*>(v), n_rows, seq_len, n_rounds, static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL(combine_compact_kernel<128>, dim3(blocks), dim3(256), 0, stream, o16, zk,
-                       static_cast<const uint16_t*>(v), n_rows, seq_len, n_rounds, static_cast<uint16_t*>(out));
-  return hipGetLastError();
 }
 
 }  // namespace rlsh

@@ -60,11 +60,12 @@ hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const vo
                           int bh, int seq_len, int d, int n_rounds, void* out, hipStream_t stream);
 
 // Compact per-round intermediates for the bf16 pipeline with 64-slot chunks:
-// o as float16 scaled by 2^-k per row, (z, k) as float pairs.
+// o as float16 scaled by 2^-k per row, (z, k) as float pairs.  Rounds
+// 0..r-2 are stored compact; the last round's launch combines all rounds in
+// place and writes `out` (mark, optional: event recorded between the two).
 bool compact_rounds_supported(bool bf16, int seq_len, int chunk_len);
-hipError_t launch_chunk_attend_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len, int d,
-                                       int n_rounds, bool causal, uint16_t* o16, float2* zk, hipStream_t stream);
-hipError_t launch_combine_compact(const uint16_t* o16, const float2* zk, const void* v, int bh, int seq_len, int d,
-                                  int n_rounds, void* out, hipStream_t stream);
+hipError_t launch_attend_combine_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len,
+                                         int d, int n_rounds, bool causal, uint16_t* o16, float2* zk, void* out,
+                                         hipStream_t stream, hipEvent_t* mark);
 
 }  // namespace rlsh

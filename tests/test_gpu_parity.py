@@ -237,6 +237,28 @@ def test_attention_workloads(nat, name):
     assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("L,d,r,causal", [
+    (1024, 64, 1, True),      # one round: the combine reduces to normalisation and the self fallback
+    (1536, 128, 3, False),    # round count without a specialised kernel, ragged run of chunks
+    (1536, 64, 5, True),
+    (1024, 128, 8, True),     # eight rounds at d = 128 (earlier rounds read inside the epilogue)
+    (2048, 64, 8, False),
+])
+def test_bf16_pipeline_round_counts(nat, L, d, r, causal):
+    """The bf16 pipeline stores rounds 0..r-2 compactly and combines them inside
+    the last round's attention launch; check it for several round counts."""
+    _say(f"[rounds] L{L} d{d} r{r} causal={causal}")
+    nb = 32
+    inp = W.custom_inputs(1, 2, L, d, nb, r, dtype="bf16", seed=L + 7 * r + d)
+    qk, v, rot = to_device(inp)
+    out = host(nat.attention(qk, v, rot, nb, 64, causal, n_rounds=r))
+    gb = host(nat.lsh_hash(qk, rot, nb, n_rounds=r))
+    x, vv = inp.qk.astype(np.float64), inp.v.astype(np.float64)
+    for h in range(2):
+        want = oracle.lsh_attention_head(x[0, h], vv[0, h], inp.rotations, nb, 64, causal, buckets=gb[0, h])["out"]
+        np.testing.assert_allclose(out[0, h], want, rtol=0, atol=TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_attend_invariant_to_order_inside_chunks(nat, dtype):
     """Shuffling the sorted slots inside each chunk leaves the output unchanged."""
