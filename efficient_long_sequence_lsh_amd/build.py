@@ -39,6 +39,9 @@ def build(verbose: bool = False) -> str:
         "-shared",
         # packed float32 ops stay off: ordinary float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in architectural VGPRs: the hash epilogue reads its 16
+        # projections per lane without a v_accvgpr_read each
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wno-unused-command-line-argument",
         "-I", os.path.join(ROOT, "include"),
         "-o", out_tmp,
