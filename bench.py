@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the workload the oracle runs for cpu_baseline")
     ap.add_argument("--quiet", action="store_true", help="only print the JSON line")
+    ap.add_argument("--accuracy-sweep", action="store_true",
+                    help="print the error of LSH attention against full shared-QK attention for several "
+                         "round and bucket counts (instead of the timing line)")
     ap.add_argument("--profile-stage", choices=["full", "hash", "sort", "attend", "combine", "copy"],
                     help="profiling mode: run the prerequisite stages once, then only this stage --steps times "
                          "(copy = a plain 256 MiB device copy for counter calibration); prints its timing")
@@ -290,6 +293,60 @@ def profile_stage(args, st, w):
                       "algorithmic": work}), flush=True)
 
 
+def accuracy_sweep(args):
+    """Error of LSH attention against full attention as rounds and buckets vary.
+
+    Both sides run in this library on the GPU: full shared-QK attention is the
+    same pipeline with one bucket and one chunk spanning the sequence (every
+    key visible, self masked unless it is the only key), whose agreement with
+    the float64 oracle the parity tests check.  Inputs: the small causal shape
+    (batch 2, 4 heads, L = 4096, d = 64, chunks of 64, float32) with iid normal
+    and with clustered (mixture) shared vectors, the latter also scaled by 3
+    (peaked attention); v iid normal.  Reported: the relative Frobenius error
+    ||out - full|| / ||full|| over all heads.  Diffuse full attention averages
+    thousands of rows of v, so its norm is small and the relative error of any
+    128-key window exceeds 1 there.
+    """
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from efficient_long_sequence_lsh_amd import _native as nat
+    from efficient_long_sequence_lsh_amd import workloads as W
+
+    if not os.path.exists(nat.LIB_PATH):
+        from efficient_long_sequence_lsh_amd import build
+
+        build.build()
+    base = W.WORKLOADS["small_4k_f32"]
+    rounds, buckets = [1, 2, 4, 8], [8, 16, 32, 64, 128]
+    rows = []
+    # (label, generator kind, factor on qk): the mixture scaled by 3 makes the
+    # attention peaked (same-centre scores ~ 81/sqrt(d)) instead of diffuse.
+    for label, kind, qk_scale in (("normal", "normal", 1.0), ("mixture", "mixture", 1.0),
+                                  ("mixture_x3", "mixture", 3.0)):
+        w0 = dataclasses.replace(base, qk_kind=kind, name=f"sweep_{kind}")
+        ref_in = W.make_inputs(dataclasses.replace(w0, n_buckets=1, n_rounds=1))
+        qk = torch.from_numpy((ref_in.qk * np.float32(qk_scale)).astype(np.float32)).cuda()
+        v = torch.from_numpy(ref_in.v).cuda()
+        full = nat.attention(qk, v, None, 1, w0.seq_len, w0.causal, n_rounds=1).double()
+        fnorm = float(torch.linalg.vector_norm(full))
+        for b in buckets:
+            for r in rounds:
+                inp = W.make_inputs(dataclasses.replace(w0, n_buckets=b, n_rounds=r))   # same qk, v; own R
+                rot = torch.from_numpy(inp.rotations).cuda()
+                out = nat.attention(qk, v, rot, b, w0.chunk_len, w0.causal, n_rounds=r).double()
+                err = float(torch.linalg.vector_norm(out - full)) / fnorm
+                rows.append({"qk": label, "n_buckets": b, "n_rounds": r, "rel_err": round(err, 5)})
+                log(args, f"[sweep] {label:10s} b={b:4d} r={r}: {err:.4f}")
+    print(json.dumps({"accuracy_sweep": rows, "shape": {"batch": base.batch, "heads": base.heads,
+                      "seq_len": base.seq_len, "d_head": base.d_head, "chunk_len": base.chunk_len,
+                      "causal": base.causal, "dtype": "f32"},
+                      "reference": "full shared-QK attention (one bucket, one chunk) in the same library"}),
+          flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -297,6 +354,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.accuracy_sweep:
+        accuracy_sweep(args)
+        return
 
     import numpy as np
     import torch

@@ -1,0 +1,44 @@
+"""More hash rounds bring LSH attention closer to full attention ("Reformer:
+The Efficient Transformer" (research summary), Key points, "Number of hash
+rounds" bullet).  Full shared-QK attention is this library's pipeline with one
+bucket and one chunk spanning the sequence; it is itself checked against the
+float64 oracle here."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from efficient_long_sequence_lsh_amd import workloads as W
+from gpu_util import ensure_library, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nat():
+    return ensure_library()
+
+
+@pytest.mark.parametrize("kind", ["normal", "mixture"])
+def test_error_against_full_attention_falls_with_rounds(nat, kind):
+    import torch
+
+    base = dataclasses.replace(W.WORKLOADS["small_4k_f32"], batch=1, heads=2, seq_len=2048, qk_kind=kind,
+                               name=f"rounds_{kind}")
+    ref_in = W.make_inputs(dataclasses.replace(base, n_buckets=1, n_rounds=1))
+    qk = torch.from_numpy(ref_in.qk).cuda()
+    v = torch.from_numpy(ref_in.v).cuda()
+    full = host(nat.attention(qk, v, None, 1, base.seq_len, True, n_rounds=1)).astype(np.float64)
+    want = oracle.lsh_attention_head(ref_in.qk[0, 0].astype(np.float64), ref_in.v[0, 0].astype(np.float64),
+                                     ref_in.rotations, 1, base.seq_len, True)["out"]
+    np.testing.assert_allclose(full[0, 0], want, rtol=0, atol=1e-4)
+    errs = []
+    for r in (1, 2, 4, 8):
+        inp = W.make_inputs(dataclasses.replace(base, n_buckets=16, n_rounds=r))
+        rot = torch.from_numpy(inp.rotations).cuda()
+        out = host(nat.attention(qk, v, rot, 16, 64, True, n_rounds=r)).astype(np.float64)
+        errs.append(float(np.linalg.norm(out - full) / np.linalg.norm(full)))
+    print(f"[rounds] {kind}: " + " ".join(f"{e:.4f}" for e in errs), flush=True)
+    assert errs[-1] < 0.8 * errs[0]
+    assert all(b <= 1.02 * a for a, b in zip(errs, errs[1:]))
