@@ -1,4 +1,5 @@
-"""Float64 CPU oracle for shared-QK LSH self-attention (test infrastructure only).
+"""Float64 CPU oracle for shared-QK LSH self-attention and local attention
+(test infrastructure only).
 
 Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
 may import this package; the library itself never does.
@@ -12,4 +13,9 @@ from .lsh_oracle import (  # noqa: F401
     lsh_attention_head,
     lsh_hash,
     lsh_sort,
+)
+from .local_oracle import (  # noqa: F401
+    local_attention,
+    local_attention_head,
+    local_window,
 )
