@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--accuracy-sweep", action="store_true",
                     help="print the error of LSH attention against full shared-QK attention for several "
                          "round and bucket counts (instead of the timing line)")
+    ap.add_argument("--local", action="store_true",
+                    help="time local (sliding-chunk) attention on the workload's shape instead (separate q, k, v; "
+                         "--local-chunk, --local-before, --local-after)")
+    ap.add_argument("--local-chunk", type=int, default=64)
+    ap.add_argument("--local-before", type=int, default=1)
+    ap.add_argument("--local-after", type=int, default=0)
     ap.add_argument("--profile-stage", choices=["full", "hash", "sort", "attend", "combine", "copy"],
                     help="profiling mode: run the prerequisite stages once, then only this stage --steps times "
                          "(copy = a plain 256 MiB device copy for counter calibration); prints its timing")
@@ -347,6 +353,53 @@ def accuracy_sweep(args):
           flush=True)
 
 
+def local_bench(args):
+    """Local (sliding-chunk) attention on the workload's shape: separate q, k, v
+    drawn iid normal, one JSON line with tokens/s and the HBM roofline.
+
+    Algorithmic bytes per token: one row each of q, k and v read and one output
+    row written (4 d e); the kernel reloads a key tile for every query tile
+    whose window covers it, which the roofline fraction then exposes.
+    """
+    import numpy as np
+    import torch
+
+    from efficient_long_sequence_lsh_amd import _native as nat
+    from efficient_long_sequence_lsh_amd import workloads as W
+
+    if not os.path.exists(nat.LIB_PATH):
+        from efficient_long_sequence_lsh_amd import build
+
+        build.build()
+    w = W.WORKLOADS[args.workload]
+    B, H, L, d = w.batch, w.heads, w.seq_len, w.d_head
+    g = np.random.default_rng(np.random.SeedSequence([20200104, 900 + w.index]))
+    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(g.standard_normal((B, H, L, d), dtype=np.float32)).to(tdtype).cuda() for _ in range(3))
+    out = torch.empty_like(v)
+    m, nb, na = args.local_chunk, args.local_before, args.local_after
+    fn = lambda: nat.local_attention(q, k, v, m, nb, na, w.causal, out=out)  # noqa: E731
+    ms = time_calls(fn, args.steps, args.warmup)
+    e = 2 if w.dtype == "bf16" else 4
+    N = B * H * L
+    bytes_ = N * 4 * d * e
+    mm = min(m, L)
+    window = min(L, (nb + 1 + na) * mm)
+    ach = bytes_ / (ms / 1e3) / 1e9
+    line = {
+        "metric": "local attention fwd tokens/sec",
+        "value": round(N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded iid normal q, k, v)",
+        "config": {"workload": f"local_{w.name}", "batch": B, "heads": H, "seq_len": L, "d_head": d, "chunk_len": m,
+                   "n_before": nb, "n_after": na, "causal": w.causal},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "local_attend_kernel", "traffic": None},
+        "flops_per_token": 4 * window * d,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -357,6 +410,9 @@ def main():
 
     if args.accuracy_sweep:
         accuracy_sweep(args)
+        return
+    if args.local:
+        local_bench(args)
         return
 
     import numpy as np

@@ -41,6 +41,7 @@ SIGNATURES = {
     "reformer_lsh_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "reformer_lsh_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
     "reformer_lsh_attention_timed": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p, _i, _p]),
+    "reformer_lsh_local_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
 }
 
 TIMED_EVENTS = 7   # RLSH_TIMED_EVENTS
@@ -218,4 +219,19 @@ def attention(qk: torch.Tensor, v: torch.Tensor, rotations: torch.Tensor | None,
                                       n_buckets, int(chunk_len), int(bool(causal)), _dev(out, "out"),
                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
     _check(st, "reformer_lsh_attention")
+    return out
+
+
+def local_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk_len: int, n_before: int, n_after: int,
+                    causal: bool, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Local (sliding-chunk) attention over separate ``q, k, v [B, H, L, d]`` -> ``out``."""
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k and v must have the same shape and dtype")
+    B, H, L, d = q.shape
+    if out is None:
+        out = torch.empty_like(v)
+    st = lib().reformer_lsh_local_attention(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), B, H, L, d,
+                                            int(chunk_len), int(n_before), int(n_after), int(bool(causal)),
+                                            _dev(out, "out"), _stream())
+    _check(st, "reformer_lsh_local_attention")
     return out

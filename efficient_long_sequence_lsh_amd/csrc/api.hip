@@ -362,4 +362,26 @@ rlsh_status_t reformer_lsh_attention_timed(const void* qk, const void* v, const 
                         causal, out, workspace, workspace_bytes, stream, events);
 }
 
+rlsh_status_t reformer_lsh_local_attention(const void* q, const void* k, const void* v, rlsh_dtype_t dtype, int batch,
+                                           int heads, int seq_len, int d_head, int chunk_len, int n_before,
+                                           int n_after, int causal, void* out, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, 1, -1, chunk_len);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (n_before < 0 || n_after < 0)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "n_before and n_after must be >= 0 (got %d, %d)", n_before, n_after);
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-null");
+  if ((st = check_aligned(q, "q")) != RLSH_OK || (st = check_aligned(k, "k")) != RLSH_OK ||
+      (st = check_aligned(v, "v")) != RLSH_OK || (st = check_aligned(out, "out")) != RLSH_OK)
+    return st;
+  // Chunks beyond the sequence do not exist: cap the overlaps (keeps the
+  // window arithmetic inside int range for any caller value).
+  const int n_chunks = seq_len / std::min(chunk_len, seq_len);
+  return hip_status(rlsh::launch_local_attend(q, k, v, dtype == RLSH_BF16, batch * heads, seq_len, d_head, chunk_len,
+                                              std::min(n_before, n_chunks), std::min(n_after, n_chunks), causal != 0,
+                                              out, stream),
+                    "reformer_lsh_local_attention");
+}
+
 }  // extern "C"

@@ -68,4 +68,8 @@ hipError_t launch_attend_combine_compact(const void* qk, const void* v, const in
                                          int d, int n_rounds, bool causal, uint16_t* o16, float2* zk, void* out,
                                          hipStream_t stream, hipEvent_t* mark);
 
+// Local (sliding-chunk) attention over separate q, k, v; out in the input dtype.
+hipError_t launch_local_attend(const void* q, const void* k, const void* v, bool bf16, int bh, int seq_len, int d,
+                               int chunk_len, int n_before, int n_after, bool causal, void* out, hipStream_t stream);
+
 }  // namespace rlsh

@@ -196,7 +196,9 @@ rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float*
  *   0 start            1 after the hash set-up kernels (rotation preparation)
  *   2 after the projection/argmax kernel       3 after the near-tie fix-up
  *   4 after the sort   5 after chunk attention 6 after the round combine
- * (with n_buckets == 1 events 1..3 are recorded where the hash would run).
+ * (with n_buckets == 1 events 1..3 are recorded where the hash would run; for
+ * bf16 inputs with 64-slot chunks the last round's attention launch does the
+ * combine, so event 5 follows rounds 0..r-2 and event 6 the last round).
  * Arguments and errors otherwise as reformer_lsh_attention; a null events
  * array or fewer than RLSH_TIMED_EVENTS entries is RLSH_ERR_INVALID_ARGUMENT.
  */
@@ -207,6 +209,29 @@ rlsh_status_t reformer_lsh_attention_timed(const void* qk, const void* v, const 
                                            int causal, void* out, void* workspace,
                                            size_t workspace_bytes, hipEvent_t* events, int n_events,
                                            hipStream_t stream);
+
+/* ---------------------------------------------------- local attention ----
+ * Local (sliding-chunk) self-attention ("The Reformer - Pushing the limits of
+ * language modeling" (summary page), Approach / What changed and Takeaways:
+ * chunks of length l_c attend to themselves plus an overlap of preceding and
+ * following chunks).
+ *
+ * q, k, v  [B, H, L, d] row-major in dtype, device memory, 16-byte aligned;
+ *          q may alias k (shared projection).
+ * Query i in chunk c = i / m', m' = min(chunk_len, L) (L a multiple of m'),
+ * attends to the keys j of chunks c - n_before .. c + n_after that exist (no
+ * wrap-around), restricted to j <= i when causal != 0, with one softmax of
+ * q_i . k_j / sqrt(d) over that window.  There is no self-mask: position i is
+ * always in its own window, so every query has a key.
+ * out      [B, H, L, d] in dtype (round to nearest even for bf16).
+ * Limits: d in {64, 128}; B*H <= 65535; B*H*L < 2^31; n_before, n_after >= 0
+ * (values beyond the number of chunks act as "all chunks").
+ * No workspace; asynchronous on `stream`.
+ */
+rlsh_status_t reformer_lsh_local_attention(const void* q, const void* k, const void* v,
+                                           rlsh_dtype_t dtype, int batch, int heads, int seq_len,
+                                           int d_head, int chunk_len, int n_before, int n_after,
+                                           int causal, void* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

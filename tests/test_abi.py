@@ -113,3 +113,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _native.lib()
+
+
+def test_local_attention_rejects_bad_arguments(lib):
+    # q, k, v, dtype, B, H, L, d, chunk_len, n_before, n_after, causal, out, stream
+    call = lib.reformer_lsh_local_attention
+    assert call(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, 32, -1, 0, 0, FAKE, None) == 1      # negative overlap
+    assert call(FAKE, FAKE, FAKE, 1, 1, 1, 128, 96, 32, 1, 0, 0, FAKE, None) == 2       # d = 96
+    assert call(None, FAKE, FAKE, 1, 1, 1, 128, 64, 32, 1, 0, 0, FAKE, None) == 1       # null q
+    assert call(FAKE, FAKE, FAKE, 1, 1, 1, 100, 64, 32, 1, 0, 0, FAKE, None) == 1       # L % chunk
+    assert call(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, 0, 1, 0, 0, FAKE, None) == 1        # chunk 0
+    assert call(FAKE + 4, FAKE, FAKE, 1, 1, 1, 128, 64, 32, 1, 0, 0, FAKE, None) == 1   # misaligned q
+    assert lib.reformer_lsh_last_error()
