@@ -19,3 +19,8 @@ from .local_oracle import (  # noqa: F401
     local_attention_head,
     local_window,
 )
+from .backward_oracle import (  # noqa: F401
+    dense_forward,
+    lsh_attention_head_grad,
+    target_counts,
+)
