@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--local", action="store_true",
                     help="time local (sliding-chunk) attention on the workload's shape instead (separate q, k, v; "
                          "--local-chunk, --local-before, --local-after)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gradients wrt qk and v for the forward's sorted order) instead")
     ap.add_argument("--local-chunk", type=int, default=64)
     ap.add_argument("--local-before", type=int, default=1)
     ap.add_argument("--local-after", type=int, default=0)
@@ -400,6 +402,62 @@ def local_bench(args):
     print(json.dumps(line), flush=True)
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def backward_bench(args):
+    """Backward pass on the workload: perm from the library's hash and sort,
+    out from its forward, dout iid normal; times reformer_lsh_attend_backward.
+
+    Work per head-token and round (all float32 MFMA): the z pass recomputes
+    S over the 2m-key window (2 * 2m * d flops), the key pass S, dP, dV and dK
+    for the 2m queries that see a key (4 * 2 * 2m * d), the query pass S, dP
+    and dQ over the window (3 * 2 * 2m * d).
+    """
+    import numpy as np
+    import torch
+
+    from efficient_long_sequence_lsh_amd import _native as nat
+    from efficient_long_sequence_lsh_amd import workloads as W
+
+    if not os.path.exists(nat.LIB_PATH):
+        from efficient_long_sequence_lsh_amd import build
+
+        build.build()
+    w = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(w)
+    if inp.qk_bits is not None:
+        qk = torch.from_numpy(inp.qk_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        v = torch.from_numpy(inp.v_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        qk = torch.from_numpy(inp.qk).cuda()
+        v = torch.from_numpy(inp.v).cuda()
+    rot = torch.from_numpy(inp.rotations).cuda()
+    perm, _ = nat.lsh_sort(nat.lsh_hash(qk, rot, w.n_buckets), w.n_buckets, inverse=False)
+    out = nat.attend(qk, v, perm, w.chunk_len, w.causal)
+    g = np.random.default_rng(np.random.SeedSequence([20200104, 950 + w.index]))
+    dout = torch.from_numpy(g.standard_normal(tuple(v.shape), dtype=np.float32)).to(v.dtype).cuda()
+    fn = lambda: nat.attend_backward(qk, v, perm, w.chunk_len, w.causal, out, dout)  # noqa: E731
+    ms = time_calls(fn, args.steps, args.warmup)
+    N = w.batch * w.heads * w.seq_len
+    win = min(2 * w.chunk_len, w.seq_len)
+    flops = N * w.n_rounds * (1 + 4 + 3) * 2 * win * w.d_head
+    ach = flops / (ms / 1e3) / 1e12
+    line = {
+        "metric": "LSH-attention backward tokens/sec (grads wrt qk and v)",
+        "value": round(w.tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 math on " + w.dtype + " inputs", "data": "synthetic (seeded)",
+        "config": {"workload": f"backward_{w.name}", "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "d_head": w.d_head, "n_buckets": w.n_buckets, "chunk_len": w.chunk_len, "n_rounds": w.n_rounds,
+                   "causal": w.causal},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_F32_PEAK_TFLOPS, 4), "kernel": "bwd_*_kernel (whole pass)",
+                     "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -413,6 +471,9 @@ def main():
         return
     if args.local:
         local_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
 
     import numpy as np

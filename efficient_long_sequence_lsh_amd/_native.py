@@ -42,6 +42,8 @@ SIGNATURES = {
     "reformer_lsh_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
     "reformer_lsh_attention_timed": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p, _i, _p]),
     "reformer_lsh_local_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
+    "reformer_lsh_attend_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "reformer_lsh_attend_backward": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
 }
 
 TIMED_EVENTS = 7   # RLSH_TIMED_EVENTS
@@ -235,3 +237,24 @@ def local_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk_len
                                             _dev(out, "out"), _stream())
     _check(st, "reformer_lsh_local_attention")
     return out
+
+
+def attend_backward(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk_len: int, causal: bool,
+                    out: torch.Tensor, dout: torch.Tensor):
+    """Gradients ``(dqk, dv)`` (float32 ``[B, H, L, d]``) of ``attend`` for a fixed sorted order."""
+    _check_pair(qk, v)
+    _check_pair(out, dout)
+    B, H, L, d = qk.shape
+    r = perm.shape[2]
+    if perm.dtype != torch.int32 or tuple(perm.shape) != (B, H, r, L):
+        raise ValueError("perm must be int32 [B, H, n_rounds, L]")
+    nbytes = int(lib().reformer_lsh_attend_backward_workspace_bytes(B, H, L, d, r, int(chunk_len)))
+    ws = _ws(nbytes, qk.device)
+    dqk = torch.empty((B, H, L, d), dtype=torch.float32, device=qk.device)
+    dv = torch.empty_like(dqk)
+    st = lib().reformer_lsh_attend_backward(_dev(qk, "qk"), _dev(v, "v"), _dtype_code(qk), _dev(perm, "perm"), B, H, L,
+                                            d, r, int(chunk_len), int(bool(causal)), _dev(out, "out"),
+                                            _dev(dout, "dout"), dqk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,
+                                            _stream())
+    _check(st, "reformer_lsh_attend_backward")
+    return dqk, dv

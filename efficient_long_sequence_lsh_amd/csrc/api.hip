@@ -384,4 +384,43 @@ rlsh_status_t reformer_lsh_local_attention(const void* q, const void* k, const v
                     "reformer_lsh_local_attention");
 }
 
+// Backward needs chunks of exactly 64 slots.
+rlsh_status_t check_backward_shape(int seq_len, int chunk_len) {
+  if (std::min(chunk_len, seq_len) != 64)
+    return fail(RLSH_ERR_UNSUPPORTED, "the backward pass needs chunks of 64 slots (chunk_len %d, seq_len %d)",
+                chunk_len, seq_len);
+  return ok();
+}
+
+size_t reformer_lsh_attend_backward_workspace_bytes(int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                                    int chunk_len) {
+  if (check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len) != RLSH_OK) return 0;
+  if (check_backward_shape(seq_len, chunk_len) != RLSH_OK) return 0;
+  return rlsh::backward_scratch_bytes(batch * heads, seq_len, n_rounds);
+}
+
+rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm,
+                                           int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                           int chunk_len, int causal, const void* out, const void* dout, float* dqk,
+                                           float* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if ((st = check_backward_shape(seq_len, chunk_len)) != RLSH_OK) return st;
+  if (qk == nullptr || v == nullptr || perm == nullptr || out == nullptr || dout == nullptr || dqk == nullptr ||
+      dv == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "qk, v, perm, out, dout, dqk and dv must be non-null");
+  if ((st = check_aligned(qk, "qk")) != RLSH_OK || (st = check_aligned(v, "v")) != RLSH_OK ||
+      (st = check_aligned(out, "out")) != RLSH_OK || (st = check_aligned(dout, "dout")) != RLSH_OK ||
+      (st = check_aligned(dqk, "dqk")) != RLSH_OK || (st = check_aligned(dv, "dv")) != RLSH_OK ||
+      (st = check_aligned(workspace, "workspace")) != RLSH_OK)
+    return st;
+  const size_t need = rlsh::backward_scratch_bytes(batch * heads, seq_len, n_rounds);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "backward workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  return hip_status(rlsh::launch_attend_backward(qk, v, dtype == RLSH_BF16, perm, batch * heads, seq_len, d_head,
+                                                 n_rounds, causal != 0, out, dout, dqk, dv, workspace, stream),
+                    "reformer_lsh_attend_backward");
+}
+
 }  // extern "C"

@@ -1,0 +1,426 @@
+// Gradients of the LSH attention forward with respect to the shared vectors
+// qk and the values v, for a given sorted order (the hash is held fixed: bucket
+// ids are piecewise constant in the inputs).
+//
+// "Reformer: The Efficient Transformer" (research summary), Key points: after
+// sorting, each chunk of m positions attends to itself and the chunk before it
+// (LSH attention bullet); a token attends to itself only when it has no other
+// target (Shared-QK bullet); several rounds are combined (Number of hash
+// rounds bullet; combined here with logsumexp weights).  With Z_i the
+// logsumexp of the scores of all (round, key) pairs query i sees, the forward
+// is out_i = sum_{rho, j} P_rho,ij v_j with P = exp(s_ij - Z_i), so with
+// D_i = dout_i . out_i:
+//   dv_j  += sum_{rho, i} P_rho,ij dout_i          (+ dout_j for self-fallback rows)
+//   dS    =  P (dout_i . v_j - D_i)
+//   dqk_i += sum dS_ij qk_j / sqrt(d)   (query role)
+//   dqk_j += sum dS_ij qk_i / sqrt(d)   (key role)
+//
+// Design for gfx950 (chunks of 64 slots; all contractions on the float32
+// MFMA 16x16x4, inputs widened to float32 in LDS):
+//   z pass      per (round, query chunk): the query's log2-domain normaliser
+//               over its window (chunks c-1 and c), written per position.
+//   stats       per position: Z (log2 domain, over rounds), D, and the
+//               accumulator initialisation dqk = 0, dv = dout on fallback rows.
+//   key pass    per round, per key chunk c: its keys are seen by the queries
+//               of chunks c and c+1; each wavefront owns 16 keys (K and V rows
+//               as MFMA B operands in registers), streams the 128 queries
+//               through LDS, and accumulates dv^T and dk^T (feature x key
+//               tiles) in registers; then adds them to the rows of its keys.
+//   query pass  per round, per query chunk c: keys of chunks c-1 and c; each
+//               wavefront owns 16 queries and accumulates dq^T.
+// Within a round every position is one key of one key chunk and one query of
+// one query chunk, so each pass has a single writer per row; the passes and
+// rounds run one after another on the stream, so the read-add-write of the
+// float32 gradient rows never races.
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <algorithm>
+#include <cmath>
+
+namespace rlsh {
+
+namespace {
+
+constexpr int kBT = 64;          // slots per chunk and per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdShape {
+  int seq_len;
+  int n_rounds;
+  int n_chunks;    // seq_len / 64
+  int causal;
+  float scale;     // 1 / sqrt(d)
+  float scale_log2;
+};
+
+template <int D>
+struct alignas(16) BwdTile {
+  static constexpr int kPitch = D + 4;   // floats per row: conflict-free column reads
+  float a[kBT * kPitch];                 // q rows (key pass) or k rows (query pass)
+  float b[kBT * kPitch];                 // dout rows (key pass) or v rows (query pass)
+  int pos[kBT];
+  int slot[kBT];
+  float z2[kBT];                         // key pass: Z of the queries (log2 domain)
+  float dd[kBT];                         // key pass: D of the queries
+};
+
+// Rows of one 64-slot chunk, gathered through perm and widened to float32.
+template <int D, bool BF16>
+__device__ __forceinline__ void stage_rows(float* dst, const void* src_raw, const int32_t* perm, int c, size_t row0) {
+  constexpr int kP = BwdTile<D>::kPitch;
+  if constexpr (BF16) {
+    const uint16_t* src = static_cast<const uint16_t*>(src_raw);
+    for (int u = threadIdx.x; u < kBT * (D / 8); u += blockDim.x) {
+      const int row = u / (D / 8), pc = u % (D / 8);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (row0 + perm[c * kBT + row]) * D + 8 * pc);
+      float* o = dst + row * kP + 8 * pc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __uint_as_float(raw[e] << 16);
+        o[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float* src = static_cast<const float*>(src_raw);
+    for (int u = threadIdx.x; u < kBT * (D / 4); u += blockDim.x) {
+      const int row = u / (D / 4), pc = u % (D / 4);
+      *reinterpret_cast<f32x4*>(dst + row * kP + 4 * pc) =
+          *reinterpret_cast<const f32x4*>(src + (row0 + perm[c * kBT + row]) * D + 4 * pc);
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, size_t i) {
+  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+
+// ------------------------------------------------------------- z pass ----
+// grid (n_chunks, bh * n_rounds); wavefront w owns queries 16w..16w+15 of the
+// chunk.  z2 = log2 sum_j 2^(s_ij * scale_log2) over the valid window keys
+// (-inf when there is none).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_z_kernel(const void* __restrict__ qk, const int32_t* __restrict__ perm_all,
+                                                    BwdShape s, float* __restrict__ z2_rounds) {
+  __shared__ BwdTile<D> sh;
+  constexpr int kP = BwdTile<D>::kPitch;
+  const int c = blockIdx.x, seg = blockIdx.y;
+  const int bh = seg / s.n_rounds;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + static_cast<size_t>(seg) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int qslot = c * kBT + 16 * wave + c16;
+  const int qpos = perm[qslot];
+  // B operand of S^T = K Q^T: lane (g, c16) holds q[c16][4kk + g].
+  float qreg[D / 4];
+#pragma unroll
+  for (int kk = 0; kk < D / 4; ++kk) qreg[kk] = load_elem<BF16>(qk, (row0 + qpos) * D + 4 * kk + g);
+  float mrun = -INFINITY, lrun = 0.0f;
+  for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
+    const int kc = c - 1 + h;
+    __syncthreads();
+    stage_rows<D, BF16>(sh.a, qk, perm, kc, row0);
+    if (threadIdx.x < kBT) {
+      sh.pos[threadIdx.x] = perm[kc * kBT + threadIdx.x];
+      sh.slot[threadIdx.x] = kc * kBT + threadIdx.x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < D / 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.a[(16 * kt + c16) * kP + 4 * kk + g], qreg[kk], acc, 0, 0, 0);
+      // lane holds S^T[key 16kt + 4g + j][query c16]
+      float tmax = -INFINITY;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * kt + 4 * g + j;
+        bool ok = sh.slot[kr] != qslot;
+        if (s.causal) ok = ok && sh.pos[kr] < qpos;
+        v[j] = ok ? acc[j] * s.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, v[j]);
+      }
+      const float mnew = fmaxf(mrun, tmax);
+      if (mnew != -INFINITY) {
+        float add = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add += exp2f(v[j] - mnew);
+        lrun = lrun * exp2f(mrun - mnew) + add;
+        mrun = mnew;
+      }
+    }
+  }
+  // Merge the four lanes (g = 0..3) that share query c16.
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    const float om = shfl_xor_f(mrun, off), ol = shfl_xor_f(lrun, off);
+    const float mnew = fmaxf(mrun, om);
+    if (mnew != -INFINITY) {
+      lrun = lrun * exp2f(mrun - mnew) + ol * exp2f(om - mnew);
+      mrun = mnew;
+    }
+  }
+  if (g == 0) z2_rounds[static_cast<size_t>(seg) * L + qpos] = (mrun == -INFINITY) ? -INFINITY : mrun + log2f(lrun);
+}
+
+// -------------------------------------------------------------- stats ----
+// One thread per position: Z (log2 domain) over rounds, D = dout . out, and
+// the gradient accumulators' initial values.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const float* __restrict__ z2_rounds, const void* __restrict__ out,
+                                                        const void* __restrict__ dout, int n_rows, int seq_len,
+                                                        int n_rounds, float* __restrict__ z2, float* __restrict__ dd,
+                                                        float* __restrict__ dqk, float* __restrict__ dv) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  const int bh = row / seq_len, pos = row - bh * seq_len;
+  float m = -INFINITY;
+  for (int r = 0; r < n_rounds; ++r) m = fmaxf(m, z2_rounds[(static_cast<size_t>(bh) * n_rounds + r) * seq_len + pos]);
+  float zz = -INFINITY;
+  if (m != -INFINITY) {
+    float sum = 0.0f;
+    for (int r = 0; r < n_rounds; ++r)
+      sum += exp2f(z2_rounds[(static_cast<size_t>(bh) * n_rounds + r) * seq_len + pos] - m);
+    zz = m + log2f(sum);
+  }
+  z2[row] = zz;
+  float acc = 0.0f;
+  for (int f = 0; f < D; ++f) {
+    const float go = load_elem<BF16>(dout, static_cast<size_t>(row) * D + f);
+    acc = fmaf(go, load_elem<BF16>(out, static_cast<size_t>(row) * D + f), acc);
+    dqk[static_cast<size_t>(row) * D + f] = 0.0f;
+    dv[static_cast<size_t>(row) * D + f] = (zz == -INFINITY) ? go : 0.0f;   // self fallback: out = v
+  }
+  dd[row] = acc;
+}
+
+// ------------------------------------------------------------ key pass ----
+// grid (n_chunks, bh) for one round.  Wavefront w owns keys 16w..16w+15 of key
+// chunk c; the queries are chunks c (own) and c+1 (next).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_key_kernel(const void* __restrict__ qk, const void* __restrict__ vv,
+                                                      const void* __restrict__ dout, const int32_t* __restrict__ perm_all,
+                                                      BwdShape s, int round, const float* __restrict__ z2,
+                                                      const float* __restrict__ dd, float* __restrict__ dqk,
+                                                      float* __restrict__ dv) {
+  __shared__ BwdTile<D> sh;
+  constexpr int kP = BwdTile<D>::kPitch;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + (static_cast<size_t>(bh) * s.n_rounds + round) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int kslot = c * kBT + 16 * wave + c16;   // this lane's key column
+  const int kpos = perm[kslot];
+  // B operands (4 features x 16 keys): lane (g, c16) holds row c16 at feature 4kk + g.
+  float kreg[D / 4], vreg[D / 4];
+#pragma unroll
+  for (int kk = 0; kk < D / 4; ++kk) {
+    kreg[kk] = load_elem<BF16>(qk, (row0 + kpos) * D + 4 * kk + g);
+    vreg[kk] = load_elem<BF16>(vv, (row0 + kpos) * D + 4 * kk + g);
+  }
+  f32x4 dvt[D / 16], dkt[D / 16];   // (feature 16dt + 4g + j, key c16)
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    dvt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dkt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const int h_end = (c + 1 < s.n_chunks) ? 2 : 1;
+  for (int h = 0; h < h_end; ++h) {
+    const int qc = c + h;
+    __syncthreads();
+    stage_rows<D, BF16>(sh.a, qk, perm, qc, row0);
+    stage_rows<D, BF16>(sh.b, dout, perm, qc, row0);
+    if (threadIdx.x < kBT) {
+      const int p = perm[qc * kBT + threadIdx.x];
+      sh.pos[threadIdx.x] = p;
+      sh.slot[threadIdx.x] = qc * kBT + threadIdx.x;
+      sh.z2[threadIdx.x] = z2[row0 + p];
+      sh.dd[threadIdx.x] = dd[row0 + p];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int qt = 0; qt < 4; ++qt) {
+      // S and dP (16 queries x 16 keys): A = q / dout rows (lane (g, c16):
+      // row c16, feature 4kk + g), B = k / v in registers.
+      f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f}, pacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < D / 4; ++kk) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.a[(16 * qt + c16) * kP + 4 * kk + g], kreg[kk], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.b[(16 * qt + c16) * kP + 4 * kk + g], vreg[kk], pacc, 0, 0, 0);
+      }
+      // lane holds (query 16qt + 4g + j, key c16)
+      float p[4], ds[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qr = 16 * qt + 4 * g + j;
+        bool ok = sh.slot[qr] != kslot;
+        if (s.causal) ok = ok && kpos < sh.pos[qr];
+        const float zq = sh.z2[qr];
+        p[j] = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
+        ds[j] = p[j] * (pacc[j] - sh.dd[qr]);
+      }
+      // dv^T += dout^T P, dk^T += q^T dS: MFMA j takes the queries 4g + j as
+      // its k index; A = (feature 16dt + c16, query 4g + j).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qr = 16 * qt + 4 * g + j;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          dvt[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.b[qr * kP + 16 * dt + c16], p[j], dvt[dt], 0, 0, 0);
+          dkt[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.a[qr * kP + 16 * dt + c16], ds[j], dkt[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // Add to the key's gradient rows: lane holds features 16dt + 4g + j of key c16.
+  float* dvr = dv + (row0 + kpos) * D;
+  float* dkr = dqk + (row0 + kpos) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(dvr + 16 * dt + 4 * g);
+    f32x4 b = *reinterpret_cast<const f32x4*>(dkr + 16 * dt + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] += dvt[dt][j];
+      b[j] = fmaf(dkt[dt][j], s.scale, b[j]);
+    }
+    *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = a;
+    *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = b;
+  }
+}
+
+// ---------------------------------------------------------- query pass ----
+// grid (n_chunks, bh) for one round.  Wavefront w owns queries 16w..16w+15 of
+// query chunk c; the keys are chunks c-1 (if any) and c.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_query_kernel(const void* __restrict__ qk, const void* __restrict__ vv,
+                                                        const void* __restrict__ dout,
+                                                        const int32_t* __restrict__ perm_all, BwdShape s, int round,
+                                                        const float* __restrict__ z2, const float* __restrict__ dd,
+                                                        float* __restrict__ dqk) {
+  __shared__ BwdTile<D> sh;
+  constexpr int kP = BwdTile<D>::kPitch;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + (static_cast<size_t>(bh) * s.n_rounds + round) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int qslot = c * kBT + 16 * wave + c16;   // this lane's query column
+  const int qpos = perm[qslot];
+  const float zq = z2[row0 + qpos];
+  const float dq = dd[row0 + qpos];
+  float qreg[D / 4], oreg[D / 4];   // B operands: q and dout of query c16 at feature 4kk + g
+#pragma unroll
+  for (int kk = 0; kk < D / 4; ++kk) {
+    qreg[kk] = load_elem<BF16>(qk, (row0 + qpos) * D + 4 * kk + g);
+    oreg[kk] = load_elem<BF16>(dout, (row0 + qpos) * D + 4 * kk + g);
+  }
+  f32x4 dqt[D / 16];   // (feature 16dt + 4g + j, query c16)
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) dqt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
+    const int kc = c - 1 + h;
+    __syncthreads();
+    stage_rows<D, BF16>(sh.a, qk, perm, kc, row0);
+    stage_rows<D, BF16>(sh.b, vv, perm, kc, row0);
+    if (threadIdx.x < kBT) {
+      sh.pos[threadIdx.x] = perm[kc * kBT + threadIdx.x];
+      sh.slot[threadIdx.x] = kc * kBT + threadIdx.x;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+      // S^T and dP^T (16 keys x 16 queries): A = k / v rows from LDS.
+      f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f}, pacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < D / 4; ++kk) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.a[(16 * kt + c16) * kP + 4 * kk + g], qreg[kk], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.b[(16 * kt + c16) * kP + 4 * kk + g], oreg[kk], pacc, 0, 0, 0);
+      }
+      // lane holds (key 16kt + 4g + j, query c16)
+      float ds[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * kt + 4 * g + j;
+        bool ok = sh.slot[kr] != qslot;
+        if (s.causal) ok = ok && sh.pos[kr] < qpos;
+        const float p = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
+        ds[j] = p * (pacc[j] - dq);
+      }
+      // dq^T += k^T dS^T: MFMA j takes keys 4g + j as its k index.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * kt + 4 * g + j;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          dqt[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.a[kr * kP + 16 * dt + c16], ds[j], dqt[dt], 0, 0, 0);
+      }
+    }
+  }
+  float* dqr = dqk + (row0 + qpos) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(dqr + 16 * dt + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = fmaf(dqt[dt][j], s.scale, a[j]);
+    *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = a;
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_typed(const void* qk, const void* v, const void* out, const void* dout, const int32_t* perm,
+                            int bh, const BwdShape& s, float* z2_rounds, float* z2, float* dd, float* dqk, float* dv,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_z_kernel<D, BF16>), dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, qk, perm, s,
+                     z2_rounds);
+  const int n_rows = bh * s.seq_len;
+  hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3((n_rows + 255) / 256), dim3(256), 0, stream, z2_rounds, out,
+                     dout, n_rows, s.seq_len, s.n_rounds, z2, dd, dqk, dv);
+  for (int r = 0; r < s.n_rounds; ++r) {
+    hipLaunchKernelGGL((bwd_key_kernel<D, BF16>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm, s, r,
+                       z2, dd, dqk, dv);
+    hipLaunchKernelGGL((bwd_query_kernel<D, BF16>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm, s,
+                       r, z2, dd, dqk);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_scratch_bytes(int bh, int seq_len, int n_rounds) {
+  const size_t n = static_cast<size_t>(bh) * seq_len;
+  return align_up(n * n_rounds * sizeof(float), 256) + 2 * align_up(n * sizeof(float), 256);
+}
+
+hipError_t launch_attend_backward(const void* qk, const void* v, bool bf16, const int32_t* perm, int bh, int seq_len,
+                                  int d, int n_rounds, bool causal, const void* out, const void* dout, float* dqk,
+                                  float* dv, void* workspace, hipStream_t stream) {
+  BwdShape s{};
+  s.seq_len = seq_len;
+  s.n_rounds = n_rounds;
+  s.n_chunks = seq_len / kBT;
+  s.causal = causal ? 1 : 0;
+  s.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+  s.scale_log2 = s.scale * kLog2e;
+  const size_t n = static_cast<size_t>(bh) * seq_len;
+  char* ws = static_cast<char*>(workspace);
+  float* z2_rounds = reinterpret_cast<float*>(ws);
+  float* z2 = reinterpret_cast<float*>(ws + align_up(n * n_rounds * sizeof(float), 256));
+  float* dd = reinterpret_cast<float*>(ws + align_up(n * n_rounds * sizeof(float), 256) + align_up(n * sizeof(float), 256));
+  if (d == 64)
+    return bf16 ? launch_bwd_typed<64, true>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream)
+                : launch_bwd_typed<64, false>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream);
+  return bf16 ? launch_bwd_typed<128, true>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream)
+              : launch_bwd_typed<128, false>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream);
+}
+
+}  // namespace rlsh

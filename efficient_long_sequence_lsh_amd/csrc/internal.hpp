@@ -72,4 +72,11 @@ hipError_t launch_attend_combine_compact(const void* qk, const void* v, const in
 hipError_t launch_local_attend(const void* q, const void* k, const void* v, bool bf16, int bh, int seq_len, int d,
                                int chunk_len, int n_before, int n_after, bool causal, void* out, hipStream_t stream);
 
+// Gradients of chunk attention + combine for a given sorted order (chunks of
+// 64 slots): dqk, dv float32 [bh, L, d]; workspace backward_scratch_bytes().
+size_t backward_scratch_bytes(int bh, int seq_len, int n_rounds);
+hipError_t launch_attend_backward(const void* qk, const void* v, bool bf16, const int32_t* perm, int bh, int seq_len,
+                                  int d, int n_rounds, bool causal, const void* out, const void* dout, float* dqk,
+                                  float* dv, void* workspace, hipStream_t stream);
+
 }  // namespace rlsh

@@ -210,6 +210,32 @@ rlsh_status_t reformer_lsh_attention_timed(const void* qk, const void* v, const 
                                            size_t workspace_bytes, hipEvent_t* events, int n_events,
                                            hipStream_t stream);
 
+/* ------------------------------------------------------------ backward ----
+ * Gradients of reformer_lsh_attend (chunk attention + logsumexp combine +
+ * self fallback) with respect to qk and v, for a given sorted order.  The
+ * bucket ids are piecewise constant in the inputs, so the order is held
+ * fixed and gradients flow through the scores and values only (Key points,
+ * LSH attention and Shared-QK bullets; the pages give no backward).
+ *
+ * qk, v, dtype, perm, sizes, chunk_len, causal: as for reformer_lsh_attend;
+ *          chunks must be exactly 64 slots (min(chunk_len, L) == 64), else
+ *          RLSH_ERR_UNSUPPORTED.
+ * out      [B, H, L, d] in dtype: the forward output for these inputs.
+ * dout     [B, H, L, d] in dtype: gradient of the loss with respect to out.
+ * dqk, dv  [B, H, L, d] float32, written (not accumulated): dqk sums the
+ *          query and key roles of each shared vector.
+ * workspace: at least reformer_lsh_attend_backward_workspace_bytes() bytes.
+ * All pointers device memory, 16-byte aligned; asynchronous on `stream`.
+ */
+size_t reformer_lsh_attend_backward_workspace_bytes(int batch, int heads, int seq_len, int d_head,
+                                                    int n_rounds, int chunk_len);
+rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_dtype_t dtype,
+                                           const int32_t* perm, int batch, int heads, int seq_len,
+                                           int d_head, int n_rounds, int chunk_len, int causal,
+                                           const void* out, const void* dout, float* dqk, float* dv,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
 /* ---------------------------------------------------- local attention ----
  * Local (sliding-chunk) self-attention ("The Reformer - Pushing the limits of
  * language modeling" (summary page), Approach / What changed and Takeaways:

@@ -1,0 +1,67 @@
+"""Gradients of chunk attention + combine on the GPU against the float64
+autograd oracle (bucket order held fixed)."""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_long_sequence_lsh_amd import workloads as W
+from gpu_util import ensure_library, host, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nat():
+    return ensure_library()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("L,d,r,nb,causal,dtype", [
+    (256, 64, 1, 8, False, "f32"),
+    (512, 64, 2, 16, True, "f32"),
+    (512, 128, 3, 8, True, "f32"),
+    (1024, 64, 2, 32, True, "bf16"),
+    (384, 128, 2, 4, False, "bf16"),
+])
+def test_backward_matches_oracle(nat, L, d, r, nb, causal, dtype):
+    import torch
+
+    _say(f"[bwd] L{L} d{d} r{r} b{nb} causal={causal} {dtype}")
+    inp = W.custom_inputs(1, 2, L, d, nb, r, dtype=dtype, seed=L + d + r)
+    qk, v, rot = to_device(inp)
+    b = nat.lsh_hash(qk, rot, nb)
+    perm, _ = nat.lsh_sort(b, nb)
+    out = nat.attend(qk, v, perm, 64, causal)
+    g = np.random.default_rng(L + 1)
+    dout_h = g.standard_normal((1, 2, L, d)).astype(np.float32)
+    if dtype == "bf16":
+        dbits = W.f32_to_bf16_bits(dout_h)
+        dout_h = W.bf16_bits_to_f32(dbits)
+        dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        dout = torch.from_numpy(dout_h).cuda()
+    dqk, dv = nat.attend_backward(qk, v, perm, 64, causal, out, dout)
+    dqk, dv = host(dqk), host(dv)
+    ph = host(perm)
+    for h in range(2):
+        _, wx, wv = oracle.lsh_attention_head_grad(inp.qk[0, h].astype(np.float64), inp.v[0, h].astype(np.float64),
+                                                   ph[0, h], 64, causal, dout_h[0, h].astype(np.float64))
+        scale = max(1.0, float(np.abs(wx).max()), float(np.abs(wv).max()))
+        tol = (1e-4 if dtype == "f32" else 2e-2) * scale
+        ex, ev = float(np.abs(dqk[0, h] - wx).max()), float(np.abs(dv[0, h] - wv).max())
+        _say(f"  head {h}: max |dqk err| {ex:.2e}  max |dv err| {ev:.2e}  (scale {scale:.2f})")
+        assert ex <= tol and ev <= tol
+
+
+def test_backward_rejects_other_chunk_lengths(nat):
+    import torch
+
+    inp = W.custom_inputs(1, 1, 256, 64, 8, 1, dtype="f32", seed=3)
+    qk, v, rot = to_device(inp)
+    perm, _ = nat.lsh_sort(nat.lsh_hash(qk, rot, 8), 8)
+    out = nat.attend(qk, v, perm, 32, False)
+    with pytest.raises(nat.LshError, match="UNSUPPORTED"):
+        nat.attend_backward(qk, v, perm, 32, False, out, torch.ones_like(out))
