@@ -323,17 +323,6 @@ struct alignas(16) Lds64 {
   int pos[(kRun64 + 1) * kKTile];   // perm of the run's chunks (and the one before)
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// gfx950 transposing LDS read: within each group of 16 lanes, lane 4k+q names
-// 4 consecutive bf16 (row k, columns 4q..4q+3 of a 4x16 block) and lane i
-// receives column i, i.e. the 4 rows' values at column i.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (s16x4 __attribute__((address_space(3)))*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
 template <int D>
 struct TileRegs {
   static constexpr int kChunks = D / 8;                  // 16-byte pieces per row

@@ -15,17 +15,21 @@
 //   dqk_i += sum dS_ij qk_j / sqrt(d)   (query role)
 //   dqk_j += sum dS_ij qk_i / sqrt(d)   (key role)
 //
-// Design for gfx950 (chunks of 64 slots; all contractions on the float32
-// MFMA 16x16x4, inputs widened to float32 in LDS):
+// Design for gfx950 (chunks of 64 slots).  bf16 inputs: S and dP on the bf16
+// MFMA 16x16x32 (products of bf16 inputs are exact in float32), P and dS
+// rounded to bf16 for the gradient contractions, whose transposed operands come
+// from the gfx950 transposing LDS read; float32 inputs: every contraction on
+// the float32 MFMA 16x16x4 with rows widened in LDS.
 //   z pass      per (round, query chunk): the query's log2-domain normaliser
 //               over its window (chunks c-1 and c), written per position.
-//   stats       per position: Z (log2 domain, over rounds), D, and the
-//               accumulator initialisation dqk = 0, dv = dout on fallback rows.
+//   stats       per position: Z (log2 domain, over rounds) and D.
 //   key pass    per round, per key chunk c: its keys are seen by the queries
 //               of chunks c and c+1; each wavefront owns 16 keys (K and V rows
 //               as MFMA B operands in registers), streams the 128 queries
 //               through LDS, and accumulates dv^T and dk^T (feature x key
-//               tiles) in registers; then adds them to the rows of its keys.
+//               tiles) in registers; then adds them to the rows of its keys
+//               (round 0 writes them, with dout added to dv on self-fallback
+//               rows, so no separate initialisation pass is needed).
 //   query pass  per round, per query chunk c: keys of chunks c-1 and c; each
 //               wavefront owns 16 queries and accumulates dq^T.
 // Within a round every position is one key of one key chunk and one query of
@@ -170,34 +174,86 @@ __global__ __launch_bounds__(256) void bwd_z_kernel(const void* __restrict__ qk,
 }
 
 // -------------------------------------------------------------- stats ----
-// One thread per position: Z (log2 domain) over rounds, D = dout . out, and
-// the gradient accumulators' initial values.
+// D/8 lanes per position (8 features each): Z (log2 domain) over rounds and
+// D = dout . out.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const float* __restrict__ z2_rounds, const void* __restrict__ out,
                                                         const void* __restrict__ dout, int n_rows, int seq_len,
-                                                        int n_rounds, float* __restrict__ z2, float* __restrict__ dd,
-                                                        float* __restrict__ dqk, float* __restrict__ dv) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= n_rows) return;
+                                                        int n_rounds, float* __restrict__ z2, float* __restrict__ dd) {
+  constexpr int kT = D / 8;
+  const int row = (blockIdx.x * blockDim.x + threadIdx.x) / kT;
+  const int sub = threadIdx.x % kT;
+  const bool live = row < n_rows;
+  const size_t r = live ? static_cast<size_t>(row) : 0;
+  float acc = 0.0f;
+  if constexpr (BF16) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(out) + r * D + 8 * sub);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(dout) + r * D + 8 * sub);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+      acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(out) + r * D + 8 * sub + 4 * h);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(dout) + r * D + 8 * sub + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(a[e], b[e], acc);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kT; off <<= 1) acc += __shfl_xor(acc, off, kT);
+  if (!live || sub != 0) return;
   const int bh = row / seq_len, pos = row - bh * seq_len;
+  const float* zr = z2_rounds + static_cast<size_t>(bh) * n_rounds * seq_len + pos;
   float m = -INFINITY;
-  for (int r = 0; r < n_rounds; ++r) m = fmaxf(m, z2_rounds[(static_cast<size_t>(bh) * n_rounds + r) * seq_len + pos]);
+  for (int k = 0; k < n_rounds; ++k) m = fmaxf(m, zr[static_cast<size_t>(k) * seq_len]);
   float zz = -INFINITY;
   if (m != -INFINITY) {
     float sum = 0.0f;
-    for (int r = 0; r < n_rounds; ++r)
-      sum += exp2f(z2_rounds[(static_cast<size_t>(bh) * n_rounds + r) * seq_len + pos] - m);
+    for (int k = 0; k < n_rounds; ++k) sum += exp2f(zr[static_cast<size_t>(k) * seq_len] - m);
     zz = m + log2f(sum);
   }
   z2[row] = zz;
-  float acc = 0.0f;
-  for (int f = 0; f < D; ++f) {
-    const float go = load_elem<BF16>(dout, static_cast<size_t>(row) * D + f);
-    acc = fmaf(go, load_elem<BF16>(out, static_cast<size_t>(row) * D + f), acc);
-    dqk[static_cast<size_t>(row) * D + f] = 0.0f;
-    dv[static_cast<size_t>(row) * D + f] = (zz == -INFINITY) ? go : 0.0f;   // self fallback: out = v
-  }
   dd[row] = acc;
+}
+
+// Add (or, in round 0, write) the key-side gradients of one key: the lane
+// holds features 16dt + 4g + j of key row kpos.  Round 0 also adds dout to dv
+// on a self-fallback row (out = v there).
+template <int D, bool BF16>
+__device__ __forceinline__ void store_key_grads(const f32x4 (&dvt)[D / 16], const f32x4 (&dkt)[D / 16], size_t row0,
+                                                int kpos, int g, int round, const float* __restrict__ z2,
+                                                const void* __restrict__ dout, float scale, float* __restrict__ dqk,
+                                                float* __restrict__ dv) {
+  float* dvr = dv + (row0 + kpos) * D;
+  float* dkr = dqk + (row0 + kpos) * D;
+  const bool fallback = round == 0 && z2[row0 + kpos] == -INFINITY;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 a = dvt[dt];
+    f32x4 b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = dkt[dt][j] * scale;
+    if (round == 0) {
+      if (fallback) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] += load_elem<BF16>(dout, (row0 + kpos) * D + 16 * dt + 4 * g + j);
+      }
+    } else {
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(dvr + 16 * dt + 4 * g);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(dkr + 16 * dt + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[j] += pa[j];
+        b[j] += pb[j];
+      }
+    }
+    *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = a;
+    *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = b;
+  }
 }
 
 // ------------------------------------------------------------ key pass ----
@@ -280,21 +336,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(const void* __restrict__ q
       }
     }
   }
-  // Add to the key's gradient rows: lane holds features 16dt + 4g + j of key c16.
-  float* dvr = dv + (row0 + kpos) * D;
-  float* dkr = dqk + (row0 + kpos) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(dvr + 16 * dt + 4 * g);
-    f32x4 b = *reinterpret_cast<const f32x4*>(dkr + 16 * dt + 4 * g);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a[j] += dvt[dt][j];
-      b[j] = fmaf(dkt[dt][j], s.scale, b[j]);
-    }
-    *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = a;
-    *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = b;
-  }
+  store_key_grads<D, BF16>(dvt, dkt, row0, kpos, g, round, z2, dout, s.scale, dqk, dv);
 }
 
 // ---------------------------------------------------------- query pass ----
@@ -376,20 +418,308 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(const void* __restrict__
   }
 }
 
+// ------------------------------------------------- bf16 MFMA variants ----
+template <int D>
+struct alignas(16) BwdTile16 {
+  static constexpr int kPitch = D + 16;   // bf16 per row: conflict-free transposing reads
+  uint16_t a[kBT * kPitch];               // q rows (key pass) or k rows (z and query passes)
+  uint16_t b[kBT * kPitch];               // dout rows (key pass) or v rows (query pass)
+  int pos[kBT];
+  int slot[kBT];
+  float z2[kBT];
+  float dd[kBT];
+};
+
+template <int D>
+__device__ __forceinline__ void stage_rows16(uint16_t* dst, const uint16_t* __restrict__ src, const int32_t* perm,
+                                             int c, size_t row0) {
+  constexpr int kP = BwdTile16<D>::kPitch;
+  for (int u = threadIdx.x; u < kBT * (D / 8); u += blockDim.x) {
+    const int row = u / (D / 8), pc = u % (D / 8);
+    *reinterpret_cast<u32x4*>(dst + row * kP + 8 * pc) =
+        *reinterpret_cast<const u32x4*>(src + (row0 + perm[c * kBT + row]) * D + 8 * pc);
+  }
+}
+
+// Row fragment of one shared vector as a bf16 MFMA operand: features
+// 32kk + 8g .. +7 of row `row`.
+template <int D>
+__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 32], const uint16_t* __restrict__ src, size_t row,
+                                               int g) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    f[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + row * D + 32 * kk + 8 * g));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* rowp, int kk, int g) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + 32 * kk + 8 * g));
+}
+
+// 16 rows x 16 rows of dot products over d features: A rows from LDS, B rows in registers.
+template <int D>
+__device__ __forceinline__ f32x4 dot_tile16(const uint16_t* arow, const bf16x8 (&b)[D / 32], int g) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag<D>(arow, kk, g), b[kk], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[2][4]) {
+  u32x4 p;
+  p[0] = pack_bf16x2(x[0][0], x[0][1]);
+  p[1] = pack_bf16x2(x[0][2], x[0][3]);
+  p[2] = pack_bf16x2(x[1][0], x[1][1]);
+  p[3] = pack_bf16x2(x[1][2], x[1][3]);
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+// Transposed operand (16 features x 32 rows) from row-major LDS rows: lane
+// (g, c16) gets feature 16dt + c16 of rows r0 + 4g + 0..3 and r0 + 16 + 4g + 0..3.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_frag_t(const uint16_t* base, int r0, int dt, int g, int c16) {
+  constexpr int kP = BwdTile16<D>::kPitch;
+  const uint16_t* p = base + (r0 + 4 * g + (c16 >> 2)) * kP + 4 * (c16 & 3) + 16 * dt;
+  const u32x2 lo = lds_read_tr16(p);
+  const u32x2 hi = lds_read_tr16(p + 16 * kP);
+  u32x4 a;
+  a[0] = lo[0];
+  a[1] = lo[1];
+  a[2] = hi[0];
+  a[3] = hi[1];
+  return __builtin_bit_cast(bf16x8, a);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_z16_kernel(const uint16_t* __restrict__ qk,
+                                                      const int32_t* __restrict__ perm_all, BwdShape s,
+                                                      float* __restrict__ z2_rounds) {
+  __shared__ BwdTile16<D> sh;
+  constexpr int kP = BwdTile16<D>::kPitch;
+  const int c = blockIdx.x, seg = blockIdx.y;
+  const int bh = seg / s.n_rounds;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + static_cast<size_t>(seg) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int qslot = c * kBT + 16 * wave + c16;
+  const int qpos = perm[qslot];
+  bf16x8 qf[D / 32];
+  load_row_frags<D>(qf, qk, row0 + qpos, g);
+  float mrun = -INFINITY, lrun = 0.0f;
+  for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
+    const int kc = c - 1 + h;
+    __syncthreads();
+    stage_rows16<D>(sh.a, qk, perm, kc, row0);
+    if (threadIdx.x < kBT) {
+      sh.pos[threadIdx.x] = perm[kc * kBT + threadIdx.x];
+      sh.slot[threadIdx.x] = kc * kBT + threadIdx.x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x4 acc = dot_tile16<D>(&sh.a[(16 * kt + c16) * kP], qf, g);   // S^T[key 16kt+4g+j][query c16]
+      float tmax = -INFINITY;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 16 * kt + 4 * g + j;
+        bool ok = sh.slot[kr] != qslot;
+        if (s.causal) ok = ok && sh.pos[kr] < qpos;
+        v[j] = ok ? acc[j] * s.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, v[j]);
+      }
+      const float mnew = fmaxf(mrun, tmax);
+      if (mnew != -INFINITY) {
+        float add = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add += exp2f(v[j] - mnew);
+        lrun = lrun * exp2f(mrun - mnew) + add;
+        mrun = mnew;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    const float om = shfl_xor_f(mrun, off), ol = shfl_xor_f(lrun, off);
+    const float mnew = fmaxf(mrun, om);
+    if (mnew != -INFINITY) {
+      lrun = lrun * exp2f(mrun - mnew) + ol * exp2f(om - mnew);
+      mrun = mnew;
+    }
+  }
+  if (g == 0) z2_rounds[static_cast<size_t>(seg) * L + qpos] = (mrun == -INFINITY) ? -INFINITY : mrun + log2f(lrun);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_key16_kernel(const uint16_t* __restrict__ qk, const uint16_t* __restrict__ vv,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const int32_t* __restrict__ perm_all, BwdShape s, int round,
+                                                        const float* __restrict__ z2, const float* __restrict__ dd,
+                                                        float* __restrict__ dqk, float* __restrict__ dv) {
+  __shared__ BwdTile16<D> sh;
+  constexpr int kP = BwdTile16<D>::kPitch;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + (static_cast<size_t>(bh) * s.n_rounds + round) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int kslot = c * kBT + 16 * wave + c16;
+  const int kpos = perm[kslot];
+  bf16x8 kf[D / 32], vf[D / 32];
+  load_row_frags<D>(kf, qk, row0 + kpos, g);
+  load_row_frags<D>(vf, vv, row0 + kpos, g);
+  f32x4 dvt[D / 16], dkt[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    dvt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dkt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const int h_end = (c + 1 < s.n_chunks) ? 2 : 1;
+  for (int h = 0; h < h_end; ++h) {
+    const int qc = c + h;
+    __syncthreads();
+    stage_rows16<D>(sh.a, qk, perm, qc, row0);
+    stage_rows16<D>(sh.b, dout, perm, qc, row0);
+    if (threadIdx.x < kBT) {
+      const int p = perm[qc * kBT + threadIdx.x];
+      sh.pos[threadIdx.x] = p;
+      sh.slot[threadIdx.x] = qc * kBT + threadIdx.x;
+      sh.z2[threadIdx.x] = z2[row0 + p];
+      sh.dd[threadIdx.x] = dd[row0 + p];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qp = 0; qp < 2; ++qp) {
+      float pv[2][4], dsv[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qt = 2 * qp + u;
+        const f32x4 sacc = dot_tile16<D>(&sh.a[(16 * qt + c16) * kP], kf, g);   // S[query 16qt+4g+j][key c16]
+        const f32x4 pacc = dot_tile16<D>(&sh.b[(16 * qt + c16) * kP], vf, g);   // dout_q . v_key
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qr = 16 * qt + 4 * g + j;
+          bool ok = sh.slot[qr] != kslot;
+          if (s.causal) ok = ok && kpos < sh.pos[qr];
+          const float zq = sh.z2[qr];
+          const float p = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
+          pv[u][j] = p;
+          dsv[u][j] = p * (pacc[j] - sh.dd[qr]);
+        }
+      }
+      // dv^T += dout^T P and dk^T += q^T dS over these 32 queries.
+      const bf16x8 bp = pack8(pv), bs = pack8(dsv);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        dvt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.b, 32 * qp, dt, g, c16), bp, dvt[dt], 0, 0, 0);
+        dkt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.a, 32 * qp, dt, g, c16), bs, dkt[dt], 0, 0, 0);
+      }
+    }
+  }
+  store_key_grads<D, true>(dvt, dkt, row0, kpos, g, round, z2, dout, s.scale, dqk, dv);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_query16_kernel(const uint16_t* __restrict__ qk,
+                                                          const uint16_t* __restrict__ vv,
+                                                          const uint16_t* __restrict__ dout,
+                                                          const int32_t* __restrict__ perm_all, BwdShape s, int round,
+                                                          const float* __restrict__ z2, const float* __restrict__ dd,
+                                                          float* __restrict__ dqk) {
+  __shared__ BwdTile16<D> sh;
+  constexpr int kP = BwdTile16<D>::kPitch;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int L = s.seq_len;
+  const int32_t* perm = perm_all + (static_cast<size_t>(bh) * s.n_rounds + round) * L;
+  const size_t row0 = static_cast<size_t>(bh) * L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int qslot = c * kBT + 16 * wave + c16;
+  const int qpos = perm[qslot];
+  const float zq = z2[row0 + qpos];
+  const float dq = dd[row0 + qpos];
+  bf16x8 qf[D / 32], of[D / 32];
+  load_row_frags<D>(qf, qk, row0 + qpos, g);
+  load_row_frags<D>(of, dout, row0 + qpos, g);
+  f32x4 dqt[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) dqt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
+    const int kc = c - 1 + h;
+    __syncthreads();
+    stage_rows16<D>(sh.a, qk, perm, kc, row0);
+    stage_rows16<D>(sh.b, vv, perm, kc, row0);
+    if (threadIdx.x < kBT) {
+      sh.pos[threadIdx.x] = perm[kc * kBT + threadIdx.x];
+      sh.slot[threadIdx.x] = kc * kBT + threadIdx.x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      float dsv[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kt = 2 * kp + u;
+        const f32x4 sacc = dot_tile16<D>(&sh.a[(16 * kt + c16) * kP], qf, g);   // S^T[key 16kt+4g+j][query c16]
+        const f32x4 pacc = dot_tile16<D>(&sh.b[(16 * kt + c16) * kP], of, g);   // v_key . dout_q
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * kt + 4 * g + j;
+          bool ok = sh.slot[kr] != qslot;
+          if (s.causal) ok = ok && sh.pos[kr] < qpos;
+          const float p = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
+          dsv[u][j] = p * (pacc[j] - dq);
+        }
+      }
+      const bf16x8 bs = pack8(dsv);   // dS^T over these 32 keys
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        dqt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.a, 32 * kp, dt, g, c16), bs, dqt[dt], 0, 0, 0);
+    }
+  }
+  float* dqr = dqk + (row0 + qpos) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(dqr + 16 * dt + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = fmaf(dqt[dt][j], s.scale, a[j]);
+    *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = a;
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch_bwd_typed(const void* qk, const void* v, const void* out, const void* dout, const int32_t* perm,
                             int bh, const BwdShape& s, float* z2_rounds, float* z2, float* dd, float* dqk, float* dv,
                             hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_z_kernel<D, BF16>), dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, qk, perm, s,
-                     z2_rounds);
+  const uint16_t* q16 = static_cast<const uint16_t*>(qk);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  const uint16_t* o16 = static_cast<const uint16_t*>(dout);
+  if constexpr (BF16)
+    hipLaunchKernelGGL(bwd_z16_kernel<D>, dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, q16, perm, s,
+                       z2_rounds);
+  else
+    hipLaunchKernelGGL((bwd_z_kernel<D, false>), dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, qk, perm, s,
+                       z2_rounds);
   const int n_rows = bh * s.seq_len;
-  hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3((n_rows + 255) / 256), dim3(256), 0, stream, z2_rounds, out,
-                     dout, n_rows, s.seq_len, s.n_rounds, z2, dd, dqk, dv);
+  const int stats_threads = n_rows * (D / 8);
+  hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3((stats_threads + 255) / 256), dim3(256), 0, stream, z2_rounds,
+                     out, dout, n_rows, s.seq_len, s.n_rounds, z2, dd);
   for (int r = 0; r < s.n_rounds; ++r) {
-    hipLaunchKernelGGL((bwd_key_kernel<D, BF16>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm, s, r,
-                       z2, dd, dqk, dv);
-    hipLaunchKernelGGL((bwd_query_kernel<D, BF16>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm, s,
-                       r, z2, dd, dqk);
+    if constexpr (BF16) {
+      hipLaunchKernelGGL(bwd_key16_kernel<D>, dim3(s.n_chunks, bh), dim3(256), 0, stream, q16, v16, o16, perm, s, r,
+                         z2, dd, dqk, dv);
+      hipLaunchKernelGGL(bwd_query16_kernel<D>, dim3(s.n_chunks, bh), dim3(256), 0, stream, q16, v16, o16, perm, s, r,
+                         z2, dd, dqk);
+    } else {
+      hipLaunchKernelGGL((bwd_key_kernel<D, false>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm, s,
+                         r, z2, dd, dqk, dv);
+      hipLaunchKernelGGL((bwd_query_kernel<D, false>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm,
+                         s, r, z2, dd, dqk);
+    }
   }
   return hipGetLastError();
 }

@@ -47,4 +47,13 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) { return __shfl
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane 4k+q names 4 consecutive b16 (row k, columns 4q..4q+3 of a 4x16
+// block) and lane i receives column i, i.e. the 4 rows' values at column i.
+typedef short lds_s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  lds_s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 }  // namespace rlsh

@@ -65,15 +65,6 @@ struct alignas(16) LocalLds<D, false> {
   float v[kLKTile * kVPitch];
 };
 
-typedef short ls16x4 __attribute__((ext_vector_type(4)));
-
-// Within each group of 16 lanes, lane 4k+q names 4 consecutive bf16 (row k,
-// columns 4q..4q+3); lane i receives column i of the 4x16 block.
-__device__ __forceinline__ u32x2 local_read_tr16(const uint16_t* p) {
-  ls16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 __attribute__((address_space(3)))*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void local_attend_kernel(const void* __restrict__ q_raw,
                                                            const void* __restrict__ k_raw,
@@ -222,8 +213,8 @@ __global__ __launch_bounds__(256) void local_attend_kernel(const void* __restric
           const uint16_t* vbase = &sh.v[(32 * kb + 4 * g + (q16 >> 2)) * Lds::kVPitch + 4 * (q16 & 3)];
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) {
-            const u32x2 lo = local_read_tr16(vbase + 16 * dt);
-            const u32x2 hi = local_read_tr16(vbase + 16 * Lds::kVPitch + 16 * dt);
+            const u32x2 lo = lds_read_tr16(vbase + 16 * dt);
+            const u32x2 hi = lds_read_tr16(vbase + 16 * Lds::kVPitch + 16 * dt);
             u32x4 a;
             a[0] = lo[0];
             a[1] = lo[1];
