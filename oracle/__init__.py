@@ -24,3 +24,7 @@ from .backward_oracle import (  # noqa: F401
     lsh_attention_head_grad,
     target_counts,
 )
+from .ff_oracle import (  # noqa: F401
+    chunked_feed_forward,
+    feed_forward,
+)
