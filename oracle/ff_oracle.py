@@ -21,10 +21,22 @@ import numpy as np
 
 
 def feed_forward(x, w1, b1, w2, b2):
-    """``x [n, d]`` -> ``[n, d]`` in float64."""
+    """``x [n, d]`` -> ``[n, d]`` in float64, one position at a time.
+
+    Each row goes through the same matrix-vector products, so the result of a
+    row does not depend on how many rows are processed together (a batched
+    matrix product may change its summation order with the batch size).
+    """
     x = np.asarray(x, np.float64)
-    h = np.maximum(x @ np.asarray(w1, np.float64).T + np.asarray(b1, np.float64), 0.0)
-    return h @ np.asarray(w2, np.float64).T + np.asarray(b2, np.float64)
+    w1 = np.asarray(w1, np.float64)
+    b1 = np.asarray(b1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    b2 = np.asarray(b2, np.float64)
+    out = np.empty((x.shape[0], w2.shape[0]), np.float64)
+    for i in range(x.shape[0]):
+        h = np.maximum(w1 @ x[i] + b1, 0.0)
+        out[i] = w2 @ h + b2
+    return out
 
 
 def chunked_feed_forward(x, w1, b1, w2, b2, chunk: int):
