@@ -48,6 +48,9 @@ def parse():
                          "--local-chunk, --local-before, --local-after)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients wrt qk and v for the forward's sorted order) instead")
+    ap.add_argument("--ff", action="store_true",
+                    help="time the chunked feed-forward layer (65536 positions, d_model 1024, d_ff 4096) instead")
+    ap.add_argument("--ff-chunk", type=int, default=8192)
     ap.add_argument("--local-chunk", type=int, default=64)
     ap.add_argument("--local-before", type=int, default=1)
     ap.add_argument("--local-after", type=int, default=0)
@@ -460,6 +463,49 @@ def backward_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def ff_bench(args):
+    """Chunked feed-forward relu(x W1^T + b1) W2^T + b2 on 65536 positions
+    (the 64K text sequence at batch 1), d_model 1024, d_ff 4096, bf16, in
+    chunks of --ff-chunk positions; 4 n d f flops per call against the bf16
+    MFMA peak.  The whole-sequence call is timed too (same result bit for bit)."""
+    import numpy as np
+    import torch
+
+    from efficient_long_sequence_lsh_amd import _native as nat
+
+    if not os.path.exists(nat.LIB_PATH):
+        from efficient_long_sequence_lsh_amd import build
+
+        build.build()
+    n, d, f = 65536, 1024, 4096
+    g = np.random.default_rng(np.random.SeedSequence([20200104, 970]))
+    x = torch.from_numpy(g.standard_normal((n, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    w1 = torch.from_numpy(g.standard_normal((f, d), dtype=np.float32) / 32.0).to(torch.bfloat16).cuda()
+    w2 = torch.from_numpy(g.standard_normal((d, f), dtype=np.float32) / 64.0).to(torch.bfloat16).cuda()
+    b1 = torch.from_numpy(0.1 * g.standard_normal(f, dtype=np.float32)).cuda()
+    b2 = torch.from_numpy(0.1 * g.standard_normal(d, dtype=np.float32)).cuda()
+    out = torch.empty_like(x)
+    flops = 4.0 * n * d * f
+    res = {}
+    for label, chunk in (("chunked", args.ff_chunk), ("whole", 0)):
+        ms = time_calls(lambda: nat.feed_forward(x, w1, b1, w2, b2, chunk_tokens=chunk, out=out),  # noqa: B023
+                        args.steps, args.warmup)
+        res[label] = {"ms": round(ms, 4), "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                      "hidden_bytes": int(nat.lib().reformer_lsh_feed_forward_workspace_bytes(n, d, f, chunk))}
+    ms = res["chunked"]["ms"]
+    ach = flops / (ms / 1e3) / 1e12
+    line = {
+        "metric": "chunked feed-forward tokens/sec", "value": round(n / (ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded)",
+        "config": {"workload": "feed_forward_64k", "n_tokens": n, "d_model": d, "d_ff": f, "chunk_tokens": args.ff_chunk},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": "linear_kernel", "traffic": None},
+        "whole_sequence": res["whole"], "chunked": res["chunked"],
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -476,6 +522,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.ff:
+        ff_bench(args)
         return
 
     import numpy as np

@@ -43,6 +43,8 @@ SIGNATURES = {
     "reformer_lsh_attention_timed": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p, _i, _p]),
     "reformer_lsh_local_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
     "reformer_lsh_attend_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "reformer_lsh_feed_forward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "reformer_lsh_feed_forward": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, _p]),
     "reformer_lsh_attend_backward": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
 }
 
@@ -258,3 +260,25 @@ def attend_backward(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk
                                             _stream())
     _check(st, "reformer_lsh_attend_backward")
     return dqk, dv
+
+
+def feed_forward(x: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: torch.Tensor,
+                 chunk_tokens: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``relu(x W1^T + b1) W2^T + b2`` over ``x [n, d_model]`` (bf16) in chunks of positions."""
+    if x.dtype != torch.bfloat16 or w1.dtype != torch.bfloat16 or w2.dtype != torch.bfloat16:
+        raise TypeError("x, w1 and w2 must be bfloat16")
+    if b1.dtype != torch.float32 or b2.dtype != torch.float32:
+        raise TypeError("b1 and b2 must be float32")
+    n, d = x.shape
+    f = w1.shape[0]
+    if tuple(w1.shape) != (f, d) or tuple(w2.shape) != (d, f) or b1.numel() != f or b2.numel() != d:
+        raise ValueError("shapes: x [n, d], w1 [f, d], b1 [f], w2 [d, f], b2 [d]")
+    nbytes = int(lib().reformer_lsh_feed_forward_workspace_bytes(n, d, f, int(chunk_tokens)))
+    ws = _ws(nbytes, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib().reformer_lsh_feed_forward(_dev(x, "x"), _dev(w1, "w1"), _dev(b1, "b1"), _dev(w2, "w2"), _dev(b2, "b2"),
+                                         n, d, f, int(chunk_tokens), _dev(out, "out"), ws.data_ptr(), nbytes,
+                                         _stream())
+    _check(st, "reformer_lsh_feed_forward")
+    return out

@@ -423,4 +423,41 @@ rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_d
                     "reformer_lsh_attend_backward");
 }
 
+rlsh_status_t check_ff_shape(int n_tokens, int d_model, int d_ff, int chunk_tokens) {
+  if (n_tokens < 1 || chunk_tokens < 0)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "n_tokens must be >= 1 and chunk_tokens >= 0 (got %d, %d)", n_tokens,
+                chunk_tokens);
+  if (d_model < 128 || d_ff < 128 || d_model % 128 != 0 || d_ff % 128 != 0)
+    return fail(RLSH_ERR_UNSUPPORTED, "d_model and d_ff must be positive multiples of 128 (got %d, %d)", d_model, d_ff);
+  return ok();
+}
+
+size_t reformer_lsh_feed_forward_workspace_bytes(int n_tokens, int d_model, int d_ff, int chunk_tokens) {
+  if (check_ff_shape(n_tokens, d_model, d_ff, chunk_tokens) != RLSH_OK) return 0;
+  return a256(rlsh::feed_forward_chunk(n_tokens, chunk_tokens) * d_ff * sizeof(uint16_t));
+}
+
+rlsh_status_t reformer_lsh_feed_forward(const void* x, const void* w1, const float* b1, const void* w2,
+                                        const float* b2, int n_tokens, int d_model, int d_ff, int chunk_tokens,
+                                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  rlsh_status_t st = check_ff_shape(n_tokens, d_model, d_ff, chunk_tokens);
+  if (st != RLSH_OK) return st;
+  if (x == nullptr || w1 == nullptr || b1 == nullptr || w2 == nullptr || b2 == nullptr || out == nullptr)
+    return fail(RLSH_ERR_INVALID_ARGUMENT, "x, w1, b1, w2, b2 and out must be non-null");
+  if ((st = check_aligned(x, "x")) != RLSH_OK || (st = check_aligned(w1, "w1")) != RLSH_OK ||
+      (st = check_aligned(b1, "b1")) != RLSH_OK || (st = check_aligned(w2, "w2")) != RLSH_OK ||
+      (st = check_aligned(b2, "b2")) != RLSH_OK || (st = check_aligned(out, "out")) != RLSH_OK ||
+      (st = check_aligned(workspace, "workspace")) != RLSH_OK)
+    return st;
+  const size_t need = reformer_lsh_feed_forward_workspace_bytes(n_tokens, d_model, d_ff, chunk_tokens);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "feed-forward workspace needs %zu bytes (got %zu)", need,
+                workspace_bytes);
+  return hip_status(rlsh::launch_feed_forward(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1), b1,
+                                              static_cast<const uint16_t*>(w2), b2, n_tokens, d_model, d_ff,
+                                              chunk_tokens, static_cast<uint16_t*>(out),
+                                              static_cast<uint16_t*>(workspace), stream),
+                    "reformer_lsh_feed_forward");
+}
+
 }  // extern "C"

@@ -79,4 +79,12 @@ hipError_t launch_attend_backward(const void* qk, const void* v, bool bf16, cons
                                   int d, int n_rounds, bool causal, const void* out, const void* dout, float* dqk,
                                   float* dv, void* workspace, hipStream_t stream);
 
+// Position-wise feed-forward y = relu(x W1^T + b1) W2^T + b2 in chunks of
+// positions (bf16 x, weights and y; float32 biases); hidden holds one chunk's
+// [chunk, d_ff] bf16 intermediate.
+size_t feed_forward_chunk(int n_tokens, int chunk_tokens);
+hipError_t launch_feed_forward(const uint16_t* x, const uint16_t* w1, const float* b1, const uint16_t* w2,
+                               const float* b2, int n_tokens, int d_model, int d_ff, int chunk_tokens, uint16_t* out,
+                               uint16_t* hidden, hipStream_t stream);
+
 }  // namespace rlsh

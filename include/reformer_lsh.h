@@ -236,6 +236,29 @@ rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_d
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 
+/* -------------------------------------------------------- feed-forward ----
+ * Position-wise feed-forward layer applied to chunk_tokens positions at a time
+ * ("Reformer: The Efficient Transformer" (research summary), Summary and Key
+ * points, reversible layers bullet: chunked feed-forward layers remove the
+ * d_ff factor from memory and give numerically identical results):
+ *   out = relu(x W1^T + b1) W2^T + b2   (the pages name no activation; ReLU)
+ *
+ * x, out   [n_tokens, d_model] bf16 row-major.
+ * w1       [d_ff, d_model] bf16, w2 [d_model, d_ff] bf16 (linear-layer layout).
+ * b1 [d_ff], b2 [d_model] float32.
+ * chunk_tokens: positions per chunk (0 = all at once); the result does not
+ *          depend on it, bit for bit.  The bf16 intermediate of one chunk
+ *          ([chunk, d_ff]) lives in the workspace: at least
+ *          reformer_lsh_feed_forward_workspace_bytes() bytes.
+ * Limits: d_model and d_ff multiples of 128.  All pointers device memory,
+ * 16-byte aligned; asynchronous on `stream`.
+ */
+size_t reformer_lsh_feed_forward_workspace_bytes(int n_tokens, int d_model, int d_ff, int chunk_tokens);
+rlsh_status_t reformer_lsh_feed_forward(const void* x, const void* w1, const float* b1, const void* w2,
+                                        const float* b2, int n_tokens, int d_model, int d_ff,
+                                        int chunk_tokens, void* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------- local attention ----
  * Local (sliding-chunk) self-attention ("The Reformer - Pushing the limits of
  * language modeling" (summary page), Approach / What changed and Takeaways:

@@ -125,3 +125,16 @@ def test_local_attention_rejects_bad_arguments(lib):
     assert call(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, 0, 1, 0, 0, FAKE, None) == 1        # chunk 0
     assert call(FAKE + 4, FAKE, FAKE, 1, 1, 1, 128, 64, 32, 1, 0, 0, FAKE, None) == 1   # misaligned q
     assert lib.reformer_lsh_last_error()
+
+
+def test_feed_forward_rejects_bad_arguments(lib):
+    # x, w1, b1, w2, b2, n_tokens, d_model, d_ff, chunk_tokens, out, ws, wsb, stream
+    call = lib.reformer_lsh_feed_forward
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 96, 256, 0, FAKE, FAKE, 1 << 30, None) == 2      # d_model 96
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 128, 200, 0, FAKE, FAKE, 1 << 30, None) == 2     # d_ff 200
+    assert call(None, FAKE, FAKE, FAKE, FAKE, 100, 128, 256, 0, FAKE, FAKE, 1 << 30, None) == 1     # null x
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 256, 0, FAKE, FAKE, 1 << 30, None) == 1       # no tokens
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 128, 256, -1, FAKE, FAKE, 1 << 30, None) == 1    # chunk < 0
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 128, 256, 0, FAKE, FAKE, 16, None) == 3          # workspace
+    assert lib.reformer_lsh_feed_forward_workspace_bytes(1000, 128, 256, 64) == 64 * 256 * 2
+    assert lib.reformer_lsh_feed_forward_workspace_bytes(1000, 128, 256, 0) >= 1000 * 256 * 2

@@ -1,0 +1,54 @@
+"""Chunked feed-forward on the GPU: against the float64 oracle, and bit-equal
+results for every chunk size ("numerically identical")."""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_long_sequence_lsh_amd import workloads as W
+from gpu_util import ensure_library, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nat():
+    return ensure_library()
+
+
+def _bf16(a):
+    import torch
+
+    bits = W.f32_to_bf16_bits(a.astype(np.float32))
+    return W.bf16_bits_to_f32(bits), torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _params(n, d, f, seed):
+    import torch
+
+    g = np.random.default_rng(seed)
+    x, xd = _bf16(g.standard_normal((n, d)))
+    w1, w1d = _bf16(g.standard_normal((f, d)) / np.sqrt(d))
+    w2, w2d = _bf16(g.standard_normal((d, f)) / np.sqrt(f))
+    b1 = (0.1 * g.standard_normal(f)).astype(np.float32)
+    b2 = (0.1 * g.standard_normal(d)).astype(np.float32)
+    return (x, w1, b1, w2, b2), (xd, w1d, torch.from_numpy(b1).cuda(), w2d, torch.from_numpy(b2).cuda())
+
+
+@pytest.mark.parametrize("n,d,f,chunk", [(300, 128, 256, 0), (1024, 256, 512, 128), (1000, 128, 384, 333)])
+def test_feed_forward_matches_oracle(nat, n, d, f, chunk):
+    h, dev = _params(n, d, f, n + d + f)
+    out = host(nat.feed_forward(*dev, chunk_tokens=chunk))
+    want = oracle.feed_forward(*h)
+    scale = max(1.0, float(np.abs(want).max()))
+    err = float(np.abs(out - want).max())
+    print(f"[ff] n{n} d{d} f{f} chunk{chunk}: max abs err {err:.3e} (scale {scale:.2f})", flush=True)
+    assert err <= 1e-2 * scale
+
+
+def test_chunking_changes_no_bit(nat):
+    import torch
+
+    _, dev = _params(1000, 256, 512, 5)
+    whole = nat.feed_forward(*dev, chunk_tokens=0)
+    for chunk in (1, 7, 64, 129, 999, 1000, 5000):
+        assert torch.equal(nat.feed_forward(*dev, chunk_tokens=chunk).view(torch.int16), whole.view(torch.int16)), chunk
