@@ -175,9 +175,19 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
   }
 }
 
+// One 16-byte piece per lane from global memory straight into LDS
+// (global_load_lds): the wavefront writes 64 consecutive pieces starting at
+// the wave-uniform address l.  The loads count against vmcnt; the workgroup
+// barrier that follows them waits for that counter to drain.
+__device__ __forceinline__ void lds_dma16(const u32x4* g, u32x4* l) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+#endif
+}
+
 // --------------------------------------------------- MFMA hash (bf16) ----
 template <int D>
-__global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(
+__global__ __launch_bounds__(kHashThreads, 4) void hash_mfma_kernel(
     const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ cmax_bits,
     HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
   constexpr int kSteps = D / 16;
@@ -238,14 +248,7 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(
     const int buf = n & 1;
     const int round = n / s.n_ctiles;
     const int t = n - round * s.n_ctiles;
-    // Prefetch the next tile into registers.
-    u32x4 pre[kPerThread];
     const bool has_next = (n + 1) < n_total;
-    if (has_next) {
-      const u32x4* src = frag + static_cast<size_t>(n + 1) * kTileVec;
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) pre[i] = src[threadIdx.x + i * kHashThreads];
-    }
 
     f32x16 acc[kStrips];
 #pragma unroll
@@ -260,6 +263,16 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(
       for (int st = 0; st < kStrips; ++st) {
         acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, xf[st][ks], acc[st], 0, 0, 0);
         acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, xf[st][ks], acc[st], 0, 0, 0);
+      }
+    }
+    // Next tile straight into the other LDS buffer (global_load_lds): each
+    // wavefront instruction fills 1 KB; the barrier below waits for it.
+    if (has_next) {
+      const u32x4* src = frag + static_cast<size_t>(n + 1) * kTileVec;
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const int chunk = i * (kHashThreads / 64) + wave;
+        lds_dma16(src + chunk * 64 + lane, &lds[buf ^ 1][chunk * 64]);
       }
     }
 
@@ -300,10 +313,6 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(
       }
     }
 
-    if (has_next) {
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) lds[buf ^ 1][threadIdx.x + i * kHashThreads] = pre[i];
-    }
     __syncthreads();
   }
   if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
