@@ -7,10 +7,14 @@
 //
 // Design for gfx950
 //   * The projection x.R is a dense contraction (tokens x d) . (d x b/2), so
-//     bf16 inputs run on MFMA (v_mfma_f32_32x32x16_bf16).  Float32 accuracy is
-//     kept by splitting R = R_hi + R_lo into two bfloat16 terms: bf16 x bf16
-//     products are exact in float32, and the split leaves a residual below
-//     2^-16 |R|.  Float32 inputs use a plain FMA kernel.
+//     bf16 inputs run on MFMA.  R = R_hi + R_lo with R_hi = bf16(R): the main
+//     term x.R_hi runs on v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products are
+//     exact in float32).  The correction x.R_lo, about 2^-9 of the result, runs
+//     on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in fp8 e4m3 and
+//     E8M0 block scales (a power of two per rotation tile for R_lo, one per
+//     32 features of a token for x), at half the cost of a bf16 pass.  Its
+//     error is bounded per token (below), so decisions stay exact.  Float32
+//     inputs use a plain FMA kernel.
 //   * The matrix product is computed transposed, D = R^T X^T, so that each lane
 //     receives 16 projections of ONE token per 32x32 tile.  Every projection is
 //     turned into an ordered 32-bit key: the float's magnitude bits shifted up
@@ -18,15 +22,20 @@
 //     A running top-two of keys per lane costs one med3 and one max per value;
 //     the two lanes sharing a token merge once per round.
 //   * The top-two keys give the two leading candidates and their gap.  When the
-//     gap is below a bound on the float32 error (Cauchy-Schwarz:
-//     |x|_2 * max_j |R_j|_2 scaled by 2^-12, plus the key truncation), the
+//     gap is below twice a bound on the error of one projection, the
 //     (position, round) is queued and a fix-up kernel re-decides it in float64
 //     between those two candidates (or over all columns when even the leading
-//     magnitude is within the bound, e.g. x = 0).
+//     magnitude is within the bound, e.g. x = 0).  By Cauchy-Schwarz, with x8
+//     and R_lo8 the fp8 operands, one projection is off by at most
+//       |x| max_j |R_j - R_hi,j - R_lo8,j| + |x - x8| max_j |R_lo8,j|
+//     plus float32 accumulation (below 2^-15 (|x| max_j |R_j| + |x8| max_j
+//     |R_lo8,j|) for up to 256 products), plus the key truncation.  The column
+//     maxima come from the set-up kernel, |x| and |x - x8| from the lane that
+//     converts x.
 //   * Rotation fragments are pre-arranged in global memory in the exact order
-//     the MFMA A operand wants them, so the cooperative copy into LDS is a
-//     straight coalesced memcpy and every wave reads 1 KB contiguous per
-//     fragment (no bank conflicts).  Tiles are double-buffered through LDS.
+//     the MFMA A operands want them, so the copy into LDS is a straight
+//     coalesced memcpy and every wave reads 1 KB contiguous per fragment (no
+//     bank conflicts).  Tiles are double-buffered through LDS.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -36,7 +45,8 @@ namespace rlsh {
 
 namespace {
 
-constexpr float kTauRel = 1.0f / 4096.0f;   // 2^-12 of |x|_2 * max_j |R_j|_2
+constexpr float kTauRel = 1.0f / 4096.0f;   // FMA path: 2^-12 of |x|_2 * max_j |R_j|_2
+constexpr float kAccRel = 1.0f / 32768.0f;  // MFMA path: float32 accumulation, 2^-15
 constexpr int kHashThreads = 256;           // 4 wavefronts
 constexpr int kStrips = 2;                  // 32-token strips per wavefront
 
@@ -85,13 +95,15 @@ __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int roun
 }
 
 // Shared decision once a token's top-two keys and |x|_2 are known.
-__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int col1, int col2, float xnorm,
-                                                 float cmax, int code_bits, int half, int tok, int seq_len,
+// tau_x bounds the error of the gap between two projections before key
+// truncation, which is added here.
+__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int col1, int col2, float tau_x,
+                                                 int code_bits, int half, int tok, int seq_len,
                                                  int n_rounds, int round, int32_t* buckets, NearTieList lst) {
   const uint32_t code_mask = ((1u << code_bits) - 1u) << 1;
   float m1 = key_magnitude(k1, code_mask);
   float m2 = key_magnitude(k2, code_mask);
-  float tau = kTauRel * xnorm * cmax + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
+  float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
   int bucket = col1 + ((k1 & 1u) ? half : 0);
   int bh = tok / seq_len, pos = tok - bh * seq_len;
   buckets[(static_cast<size_t>(bh) * n_rounds + round) * seq_len + pos] = bucket;
@@ -99,52 +111,145 @@ __device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int c
   if (full || (m1 - m2) <= tau) push_near_tie(lst, tok, round, full, col1, col2);
 }
 
+// MFMA path: twice the per-projection bound (see the top of this file), with
+// a 2^-10 margin for the float32 evaluation of the bound itself.
+__device__ __forceinline__ float split_gap_bound(float xnorm, float xerr, float cmax, float rho1, float rho2) {
+  const float acc = kAccRel * (xnorm * cmax + (xnorm + xerr) * rho2);
+  return 2.0f * (xnorm * rho1 + xerr * rho2 + acc) * (1.0f + 1.0f / 1024.0f);
+}
+
+// Column-norm maxima per round, as float bits in [3][n_rounds]:
+// max_j |R_j|, max_j |R_j - R_hi,j - R_lo8,j|, max_j |R_lo8,j|.
+enum { kBoundCmax = 0, kBoundRes = 1, kBoundLo = 2, kBoundTerms = 3 };
+
 // ------------------------------------------------------ preparation ----
 // Zero the per-round column-norm maxima and the caller's near-tie total.
-__global__ void hash_init_kernel(uint32_t* cmax_bits, int n_rounds, int32_t* n_near_ties) {
-  for (int t = threadIdx.x; t < n_rounds; t += blockDim.x) cmax_bits[t] = 0u;
+__global__ void hash_init_kernel(uint32_t* bound_bits, int n_rounds, int32_t* n_near_ties) {
+  for (int t = threadIdx.x; t < kBoundTerms * n_rounds; t += blockDim.x) bound_bits[t] = 0u;
   if (threadIdx.x == 0 && n_near_ties != nullptr) *n_near_ties = 0;
 }
 
+// sqrt of a float64 sum of squares as float, rounded up (one float rounding,
+// at most 2^-24 relative, covered by the factor).
+__device__ __forceinline__ uint32_t norm_bits_up(double sum) {
+  return __float_as_uint(static_cast<float>(sqrt(sum)) * 1.0000005f);
+}
+
+// Largest value of each lane's group of 32 lanes into *dst (atomic max of
+// non-negative float bits).
+__device__ __forceinline__ void max32_to(uint32_t bits, uint32_t* dst) {
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) bits = max(bits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), off, 32)));
+  if ((threadIdx.x & 31) == 0) atomicMax(dst, bits);
+}
+
+// Fragment tile layout (16-byte units) for one (round, tile of 32 columns):
+//   [ks * 64 + l], ks < D/16: bf16 R_hi[k][c], c = 32t + l%32,
+//       k = 16ks + 8(l/32) + 0..7 (A operand of v_mfma_f32_32x32x16_bf16);
+//   [D * 4 + p * 64 + l], p = 2kb + j < D/32: fp8 R_lo[k][c] * 2^ea,
+//       k = 64kb + 32j + 16(l/32) + 0..15 (bytes 16j..16j+15 of the 32-byte A
+//       operand of the fp8 MFMA step kb).
+// The scaled MFMA pairs byte b of lane l with byte b of the B operand's lane
+// of the same l/32, and takes the E8M0 scale of bytes 16j..16j+15 (both lane
+// halves) from the lane 32j + row: so a block of 32 consecutive features
+// k = 64kb + 32j + 0..31 shares one scale.
+template <int D>
+struct FragTile {
+  static constexpr int kHiSteps = D / 16;              // bf16 MFMA k-steps
+  static constexpr int kLoSteps = D / 64;              // fp8 MFMA k-steps
+  static constexpr int kHiVec = kHiSteps * 64;
+  static constexpr int kVec = kHiVec + kLoSteps * 2 * 64;
+};
+
 // Per-call set-up, one workgroup per (tile of 32 rotation columns, round):
-//  - (FRAG) split-bf16 fragments of R in MFMA A-operand order: fragment
-//    (round r, tile t, k-step ks, term, lane l) holds, for column
-//    c = 32t + l%32 and k0 = 16ks + 8(l/32), the 8 values R[r][k0 + e][c]
-//    (zero for c >= half) as bf16 hi (term 0) or lo = bf16(R - hi) (term 1);
+//  - (FRAG) the fragment tile above, with R_hi = bf16(R) (round to nearest
+//    even), R_lo = R - R_hi (exact in float32) and ea the power of two that
+//    puts the tile's largest |R_lo| into [128, 256) (fp8 e4m3 tops out at
+//    448); the tile's E8M0 scale byte 127 - ea goes to lo_scale[round][tile];
 //  - R transposed to float32 [round][column][k], so that the fix-up reads a
 //    column as one contiguous row;
-//  - column norms (float64 sums, rounded up) folded into a per-round max.
+//  - per-round maxima over columns of |R_j|, and (FRAG) of
+//    |R_j - R_hi,j - R_lo8,j| and |R_lo8,j| (float64 sums, rounded up).
 template <int D, bool FRAG>
-__global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_ctiles,
-                                                           u32x4* __restrict__ frag, float* __restrict__ rt,
-                                                           uint32_t* __restrict__ cmax_bits) {
-  constexpr int kSteps = D / 16;
+__global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_rounds,
+                                                           int n_ctiles, u32x4* __restrict__ frag,
+                                                           float* __restrict__ rt, uint32_t* __restrict__ bound_bits,
+                                                           uint32_t* __restrict__ lo_scale) {
+  using FT = FragTile<D>;
   constexpr int kGroups = 8;               // k-ranges per column
   constexpr int kPerG = D / kGroups;       // 8 or 16 values
+  constexpr int kLoUnits = D / 16;         // 16-value k-ranges per column in the fp8 fragments
   __shared__ double part[kGroups][32];
+  __shared__ double part_res[kLoUnits][32];
+  __shared__ double part_lo[kLoUnits][32];
+  __shared__ uint32_t lo_max_bits;
+  __shared__ float tile_r[D][33];          // the tile's 32 columns (zero past half), one coalesced read
   const int t = blockIdx.x, r = blockIdx.y;
   const float* R = rot + static_cast<size_t>(r) * D * half;
-  if (FRAG) {
-    for (int u = threadIdx.x; u < kSteps * 64; u += blockDim.x) {
-      const int ks = u / 64, l = u % 64;
-      const int c = 32 * t + (l & 31);
-      const int k0 = 16 * ks + 8 * (l >> 5);
-      u32x4 hi, lo;
+  {
+    // all loads in flight before the first LDS store (launched with 256 threads)
+    constexpr int kPer = D * 32 / 256;
+    const int cl = threadIdx.x % 32, c = 32 * t + cl;
+    float v[kPer];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float v0 = 0.0f, v1 = 0.0f;
-        if (c < half) {
-          v0 = R[static_cast<size_t>(k0 + e) * half + c];
-          v1 = R[static_cast<size_t>(k0 + e + 1) * half + c];
+    for (int i = 0; i < kPer; ++i) v[i] = c < half ? R[static_cast<size_t>(threadIdx.x / 32 + 8 * i) * half + c] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) tile_r[threadIdx.x / 32 + 8 * i][cl] = v[i];
+  }
+  if (threadIdx.x == 0) lo_max_bits = 0u;
+  __syncthreads();
+  auto rval = [&](int k, int cl) -> float { return tile_r[k][cl]; };
+  auto lo_of = [](float v) -> float { return v - bf16_to_f32(f32_to_bf16_rne(v)); };
+  if (FRAG) {
+    uint32_t m = 0u;
+    for (int u = threadIdx.x; u < D * 32; u += blockDim.x) m = max(m, __float_as_uint(fabsf(lo_of(rval(u / 32, u % 32)))));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, shfl_xor_u(m, off));
+    if ((threadIdx.x & 63) == 0) atomicMax(&lo_max_bits, m);
+    __syncthreads();
+    const uint32_t mb = lo_max_bits;
+    const int ea = mb == 0u ? 0 : min(134 - static_cast<int>(mb >> 23), 127);
+    if (threadIdx.x == 0) lo_scale[static_cast<size_t>(r) * n_ctiles + t] = static_cast<uint32_t>(127 - ea);
+    u32x4* tile = frag + (static_cast<size_t>(r) * n_ctiles + t) * FT::kVec;
+    for (int u = threadIdx.x; u < FT::kHiVec; u += blockDim.x) {
+      const int ks = u / 64, l = u % 64;
+      const int c = l & 31;
+      const int k0 = 16 * ks + 8 * (l >> 5);
+      u32x4 hi;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        hi[e / 2] = static_cast<uint32_t>(f32_to_bf16_rne(rval(k0 + e, c))) |
+                    (static_cast<uint32_t>(f32_to_bf16_rne(rval(k0 + e + 1, c))) << 16);
+      tile[u] = hi;
+    }
+    for (int u = threadIdx.x; u < FT::kLoSteps * 128; u += blockDim.x) {
+      const int piece = u / 64, l = u % 64;
+      const int c = l & 31;
+      const int k0 = 32 * piece + 16 * (l >> 5);
+      u32x4 q;
+      double s_res = 0.0, s_lo = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = lo_of(rval(k0 + 4 * e + i, c));
+        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(lo[0], ea), ldexpf(lo[1], ea), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(lo[2], ea), ldexpf(lo[3], ea), w, true);
+        q[e] = w;
+        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+        const float dq[4] = {d01[0], d01[1], d23[0], d23[1]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double lo8 = ldexp(static_cast<double>(dq[i]), -ea);
+          const double res = static_cast<double>(lo[i]) - lo8;
+          s_res += res * res;
+          s_lo += lo8 * lo8;
         }
-        const uint16_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
-        const uint16_t l0 = f32_to_bf16_rne(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16_rne(v1 - bf16_to_f32(h1));
-        hi[e / 2] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-        lo[e / 2] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
       }
-      const size_t base = (((static_cast<size_t>(r) * n_ctiles + t) * kSteps + ks) * 2) * 64 + l;
-      frag[base] = hi;
-      frag[base + 64] = lo;
+      tile[FT::kHiVec + u] = q;
+      part_res[2 * piece + (l >> 5)][l & 31] = s_res;
+      part_lo[2 * piece + (l >> 5)][l & 31] = s_lo;
     }
   }
   const int cl = threadIdx.x & 31, g = threadIdx.x >> 5;
@@ -154,7 +259,7 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
     float v[kPerG];
 #pragma unroll
     for (int i = 0; i < kPerG; ++i) {
-      v[i] = R[static_cast<size_t>(g * kPerG + i) * half + c];
+      v[i] = rval(g * kPerG + i, cl);
       acc += static_cast<double>(v[i]) * static_cast<double>(v[i]);
     }
     f32x4* dst = reinterpret_cast<f32x4*>(rt + (static_cast<size_t>(r) * half + c) * D + g * kPerG);
@@ -167,11 +272,17 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
     double sum = 0.0;
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) sum += part[i][threadIdx.x];
-    uint32_t bits = 0u;
-    if (c < half) bits = __float_as_uint(static_cast<float>(sqrt(sum)) * 1.0000005f);   // round up slightly
+    max32_to(c < half ? norm_bits_up(sum) : 0u, bound_bits + kBoundCmax * n_rounds + r);
+    if (FRAG) {
+      double sr = 0.0, sl = 0.0;
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) bits = max(bits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), off, 32)));
-    if (threadIdx.x == 0) atomicMax(cmax_bits + r, bits);
+      for (int i = 0; i < kLoUnits; ++i) {
+        sr += part_res[i][threadIdx.x];
+        sl += part_lo[i][threadIdx.x];
+      }
+      max32_to(norm_bits_up(sr), bound_bits + kBoundRes * n_rounds + r);
+      max32_to(norm_bits_up(sl), bound_bits + kBoundLo * n_rounds + r);
+    }
   }
 }
 
@@ -186,37 +297,103 @@ __device__ __forceinline__ void lds_dma16(const u32x4* g, u32x4* l) {
 }
 
 // --------------------------------------------------- MFMA hash (bf16) ----
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// fp8 B operand of one token for fp8 MFMA step kb: this lane (half g = lane/32)
+// converts features k = 64kb + 32j + 16g + 0..15 (j = 0, 1) into bytes
+// 16j..16j+15.  Block j (features 64kb + 32j + 0..31, split over the two lanes
+// of the token) is scaled by 2^e_j, which puts its largest |x| into [128, 256);
+// the lane of half g returns block g's E8M0 scale byte.  Adds this lane's share
+// of |x - x8|^2 (exact differences: x has 8 significant bits, x8 is x rounded
+// to 4) to *err.
 template <int D>
-__global__ __launch_bounds__(kHashThreads, 4) void hash_mfma_kernel(
-    const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ cmax_bits,
-    HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
-  constexpr int kSteps = D / 16;
-  constexpr int kTileVec = kSteps * 2 * 64;                   // 16-byte units per fragment tile
-  constexpr int kPerThread = kTileVec / kHashThreads;
-  static_assert(kTileVec % kHashThreads == 0, "tile copy must divide evenly");
-  __shared__ u32x4 lds[2][kTileVec];
+__device__ __forceinline__ i32x8 x_to_fp8(const uint16_t* __restrict__ xrow, bool live, int kb, int g, int* scale,
+                                          float* err) {
+  u32x4 raw[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      raw[j][h] = u32x4{0u, 0u, 0u, 0u};
+      if (live) raw[j][h] = *reinterpret_cast<const u32x4*>(xrow + 64 * kb + 32 * j + 16 * g + 8 * h);
+    }
+  int ej[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t m = 0u;   // bf16 magnitudes order as integers
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = max(m, max(raw[j][h][e] & 0x7fffu, (raw[j][h][e] >> 16) & 0x7fffu));
+    m = max(m, shfl_xor_u(m, 32));
+    ej[j] = m == 0u ? 0 : min(134 - static_cast<int>(m >> 7), 127);
+  }
+  *scale = 127 - (g == 0 ? ej[0] : ej[1]);
+  i32x8 out;
+  float acc = *err;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float x0 = __uint_as_float(raw[j][h][e] << 16), x1 = __uint_as_float(raw[j][h][e] & 0xffff0000u);
+        const float x2 = __uint_as_float(raw[j][h][e + 1] << 16), x3 = __uint_as_float(raw[j][h][e + 1] & 0xffff0000u);
+        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x0, ej[j]), ldexpf(x1, ej[j]), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x2, ej[j]), ldexpf(x3, ej[j]), w, true);
+        out[4 * j + 2 * h + e / 2] = static_cast<int>(w);
+        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+        const float r0 = x0 - ldexpf(d01[0], -ej[j]), r1 = x1 - ldexpf(d01[1], -ej[j]);
+        const float r2 = x2 - ldexpf(d23[0], -ej[j]), r3 = x3 - ldexpf(d23[1], -ej[j]);
+        acc = fmaf(r0, r0, acc);
+        acc = fmaf(r1, r1, acc);
+        acc = fmaf(r2, r2, acc);
+        acc = fmaf(r3, r3, acc);
+      }
+  *err = acc;
+  return out;
+}
+
+template <int D>
+__global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
+    const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ bound_bits,
+    const uint32_t* __restrict__ lo_scale, HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
+  using FT = FragTile<D>;
+  constexpr int kSteps = FT::kHiSteps;
+  constexpr int kLoSteps = FT::kLoSteps;
+  constexpr int kTileVec = FT::kVec;                 // 16-byte units per fragment tile
+  constexpr int kChunks = kTileVec / 64;             // 1 KB wavefront copies per tile
+  constexpr int kWaves = kHashThreads / 64;
+  static_assert(kTileVec % 64 == 0, "tile copy works in 1 KB pieces");
+  __shared__ u32x4 lds0[kTileVec];   // two separate buffers, so that the compiler can tell
+  __shared__ u32x4 lds1[kTileVec];   // the copy into one from the reads of the other
   __shared__ int ntie;
-  static_assert(kHashThreads / 64 * 32 * kStrips == kTokensPerBlock, "near-tie regions assume 256 tokens per block");
+  static_assert(kWaves * 32 * kStrips == kTokensPerBlock, "near-tie regions assume 256 tokens per block");
   if (threadIdx.x == 0) ntie = 0;
   lst.lds_count = &ntie;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half_sel = lane >> 5;
-  const int tok_base = (blockIdx.x * (kHashThreads / 64) + wave) * (32 * kStrips);
+  const int tok_base = (blockIdx.x * kWaves + wave) * (32 * kStrips);
 
-  // X^T operand (B): lane holds token (lane % 32), k = 16ks + 8*(lane/32) .. +7.
+  // B operands.  bf16: lane holds token (lane % 32), k = 16ks + 8*(lane/32) .. +7.
+  // fp8: see x_to_fp8.  |x| and |x - x8| per token, rounded up.
   bf16x8 xf[kStrips][kSteps];
-  float xsq[kStrips];
+  i32x8 x8[kStrips][kLoSteps];
+  int xs8[kStrips][kLoSteps];
+  float xsq[kStrips], xer[kStrips];
 #pragma unroll
   for (int st = 0; st < kStrips; ++st) {
-    int tok = tok_base + 32 * st + (lane & 31);
+    const int tok = tok_base + 32 * st + (lane & 31);
+    const bool live = tok < s.n_tokens;
+    const uint16_t* xrow = qk + static_cast<size_t>(live ? tok : 0) * D;
     float acc = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (tok < s.n_tokens)
-        raw = *reinterpret_cast<const u32x4*>(qk + static_cast<size_t>(tok) * D + 16 * ks + 8 * half_sel);
+      if (live) raw = *reinterpret_cast<const u32x4*>(xrow + 16 * ks + 8 * half_sel);
       xf[st][ks] = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -225,17 +402,19 @@ __global__ __launch_bounds__(kHashThreads, 4) void hash_mfma_kernel(
         acc = fmaf(b, b, acc);
       }
     }
+    float err = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < kLoSteps; ++kb) x8[st][kb] = x_to_fp8<D>(xrow, live, kb, half_sel, &xs8[st][kb], &err);
     acc += shfl_xor_f(acc, 32);
-    xsq[st] = sqrtf(acc) * 1.0000005f;
+    err += shfl_xor_f(err, 32);
+    // float32 sums of at most 256 squares: relative error below 2^-16
+    xsq[st] = sqrtf(acc) * (1.0f + 1.0f / 65536.0f);
+    xer[st] = sqrtf(err) * (1.0f + 1.0f / 65536.0f);
   }
 
   const int n_total = s.n_rounds * s.n_ctiles;
   // Prologue: tile 0 into buffer 0.
-  {
-    const u32x4* src = frag;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) lds[0][threadIdx.x + i * kHashThreads] = src[threadIdx.x + i * kHashThreads];
-  }
+  for (int i = threadIdx.x; i < kTileVec; i += kHashThreads) lds0[i] = frag[i];
   __syncthreads();
 
   const uint32_t code_mask = ((1u << s.code_bits) - 1u) << 1;
@@ -244,39 +423,39 @@ __global__ __launch_bounds__(kHashThreads, 4) void hash_mfma_kernel(
 #pragma unroll
   for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; }
 
-  for (int n = 0; n < n_total; ++n) {
-    const int buf = n & 1;
-    const int round = n / s.n_ctiles;
-    const int t = n - round * s.n_ctiles;
-    const bool has_next = (n + 1) < n_total;
-
-    f32x16 acc[kStrips];
+  // Projections of tile n (lds buffer n & 1) into acc.
+  auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur, int n) {
+    const int sa = static_cast<int>(lo_scale[n]);
 #pragma unroll
     for (int st = 0; st < kStrips; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[st][i] = 0.0f;
+    // The small x.R_lo term first: the last writer of acc is then a bf16 MFMA,
+    // whose result latency the key extraction that reads acc is scheduled for.
+#pragma unroll
+    for (int kb = 0; kb < kLoSteps; ++kb) {
+      const u32x4 p0 = cur[FT::kHiVec + (2 * kb) * 64 + lane];
+      const u32x4 p1 = cur[FT::kHiVec + (2 * kb + 1) * 64 + lane];
+      const i32x8 a_lo = {static_cast<int>(p0[0]), static_cast<int>(p0[1]), static_cast<int>(p0[2]),
+                          static_cast<int>(p0[3]), static_cast<int>(p1[0]), static_cast<int>(p1[1]),
+                          static_cast<int>(p1[2]), static_cast<int>(p1[3])};
+#pragma unroll
+      for (int st = 0; st < kStrips; ++st)
+        acc[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a_lo, x8[st][kb], acc[st], 0, 0, 0, sa, 0,
+                                                                  xs8[st][kb]);
+    }
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      bf16x8 a_hi = __builtin_bit_cast(bf16x8, lds[buf][(ks * 2 + 0) * 64 + lane]);
-      bf16x8 a_lo = __builtin_bit_cast(bf16x8, lds[buf][(ks * 2 + 1) * 64 + lane]);
+      const bf16x8 a_hi = __builtin_bit_cast(bf16x8, cur[ks * 64 + lane]);
 #pragma unroll
-      for (int st = 0; st < kStrips; ++st) {
+      for (int st = 0; st < kStrips; ++st)
         acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, xf[st][ks], acc[st], 0, 0, 0);
-        acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, xf[st][ks], acc[st], 0, 0, 0);
-      }
     }
-    // Next tile straight into the other LDS buffer (global_load_lds): each
-    // wavefront instruction fills 1 KB; the barrier below waits for it.
-    if (has_next) {
-      const u32x4* src = frag + static_cast<size_t>(n + 1) * kTileVec;
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int chunk = i * (kHashThreads / 64) + wave;
-        lds_dma16(src + chunk * 64 + lane, &lds[buf ^ 1][chunk * 64]);
-      }
-    }
-
-    // Keys: acc[i] is the projection on column 32t + 8(i/4) + 4*half_sel + i%4.
+  };
+  // Keys of tile n from acc: acc[i] is the projection on column
+  // 32t + 8(i/4) + 4*half_sel + i%4.
+  auto keys_tile = [&](const f32x16 (&acc)[kStrips], int n) {
+    const int t = n % s.n_ctiles;
     const uint32_t tile_code = (static_cast<uint32_t>(t) << 5) | (static_cast<uint32_t>(half_sel) << 4);
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
@@ -290,30 +469,58 @@ __global__ __launch_bounds__(kHashThreads, 4) void hash_mfma_kernel(
       }
       top2_merge(k1[st], k2[st], t1 | (tile_code << 1), t2 | (tile_code << 1));
     }
-
-    if (t == s.n_ctiles - 1) {
-      // End of a round: merge the two lanes that share each token, decide, flag.
-      const float cmax = __uint_as_float(cmax_bits[round]);
+  };
+  // After the last tile of a round: merge the two lanes that share each
+  // token, decide, flag near-ties.
+  auto round_end = [&](int n) {
+    const int round = n / s.n_ctiles;
+    if (n - round * s.n_ctiles != s.n_ctiles - 1) return;
+    const float cmax = __uint_as_float(bound_bits[kBoundCmax * s.n_rounds + round]);
+    const float rho1 = __uint_as_float(bound_bits[kBoundRes * s.n_rounds + round]);
+    const float rho2 = __uint_as_float(bound_bits[kBoundLo * s.n_rounds + round]);
 #pragma unroll
-      for (int st = 0; st < kStrips; ++st) {
-        uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32);
-        top2_merge(k1[st], k2[st], o1, o2);
-        int tok = tok_base + 32 * st + lane;
-        if (lane < 32 && tok < s.n_tokens) {
-          uint32_t c1 = (k1[st] & code_mask) >> 1, c2 = (k2[st] & code_mask) >> 1;
-          auto col_of = [](uint32_t c) {
-            uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
-            return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
-          };
-          decide_and_store(k1[st], k2[st], col_of(c1), col_of(c2), xsq[st], cmax, s.code_bits, s.half, tok,
-                           s.seq_len, s.n_rounds, round, buckets, lst);
-        }
-        k1[st] = 0u;
-        k2[st] = 0u;
+    for (int st = 0; st < kStrips; ++st) {
+      uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32);
+      top2_merge(k1[st], k2[st], o1, o2);
+      int tok = tok_base + 32 * st + lane;
+      if (lane < 32 && tok < s.n_tokens) {
+        uint32_t c1 = (k1[st] & code_mask) >> 1, c2 = (k2[st] & code_mask) >> 1;
+        auto col_of = [](uint32_t c) {
+          uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
+          return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
+        };
+        decide_and_store(k1[st], k2[st], col_of(c1), col_of(c2), split_gap_bound(xsq[st], xer[st], cmax, rho1, rho2),
+                         s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
       }
+      k1[st] = 0u;
+      k2[st] = 0u;
     }
+  };
+  // Tile n + 1 straight into the idle LDS buffer (global_load_lds): each
+  // wavefront instruction fills 1 KB.  Issued before tile n's MFMAs, so the
+  // copy overlaps them; the barrier at the end of the step waits for it.
+  // After the last tile the copy repeats it (no branch).
+  auto dma_next = [&](u32x4* dst, int n) {
+    const u32x4* src = frag + static_cast<size_t>(min(n + 1, n_total - 1)) * kTileVec;
+#pragma unroll
+    for (int i = 0; i < (kChunks + kWaves - 1) / kWaves; ++i) {
+      const int chunk = i * kWaves + wave;
+      if (kChunks % kWaves == 0 || chunk < kChunks) lds_dma16(src + chunk * 64 + lane, dst + chunk * 64);
+    }
+  };
 
-    __syncthreads();
+  for (int n = 0; n < n_total; ++n) {
+    f32x16 acc[kStrips];
+    if ((n & 1) == 0) {
+      dma_next(lds1, n);
+      mfma_tile(acc, lds0, n);
+    } else {
+      dma_next(lds0, n);
+      mfma_tile(acc, lds1, n);
+    }
+    keys_tile(acc, n);
+    round_end(n);
+    __syncthreads();   // also makes every wavefront's near-tie pushes visible to the count below
   }
   if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
 }
@@ -360,8 +567,8 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
     }
     if (live) {
       int c1 = static_cast<int>((k1 & code_mask) >> 1), c2 = static_cast<int>((k2 & code_mask) >> 1);
-      decide_and_store(k1, k2, c1, c2, xnorm, __uint_as_float(cmax_bits[round]), s.code_bits, s.half, tok,
-                       s.seq_len, s.n_rounds, round, buckets, lst);
+      decide_and_store(k1, k2, c1, c2, kTauRel * xnorm * __uint_as_float(cmax_bits[kBoundCmax * s.n_rounds + round]),
+                       s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
   __syncthreads();
@@ -489,13 +696,14 @@ HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds
 
 HashScratch hash_scratch(const HashShape& s) {
   HashScratch h{};
-  h.frag_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * 32 * s.d * 2 * sizeof(uint16_t), 256);
+  // per tile: bf16 R_hi (2 bytes) and fp8 R_lo (1 byte) for 32 columns x d
+  h.frag_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * 32 * s.d * 3, 256);
   h.rt_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.half * s.d * sizeof(float), 256);
-  h.cmax_bytes = align_up(static_cast<size_t>(s.n_rounds) * sizeof(uint32_t), 256);
+  h.bound_bytes = align_up(static_cast<size_t>(s.n_rounds) * (kBoundTerms + s.n_ctiles) * sizeof(uint32_t), 256);
   const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
   h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
   h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
-  h.total = h.frag_bytes + h.rt_bytes + h.cmax_bytes + h.counter_bytes + h.list_bytes;
+  h.total = h.frag_bytes + h.rt_bytes + h.bound_bytes + h.counter_bytes + h.list_bytes;
   return h;
 }
 
@@ -514,8 +722,9 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   ws += h.frag_bytes;
   float* rt = reinterpret_cast<float*>(ws);
   ws += h.rt_bytes;
-  uint32_t* cmax = reinterpret_cast<uint32_t*>(ws);
-  ws += h.cmax_bytes;
+  uint32_t* bound = reinterpret_cast<uint32_t*>(ws);               // [kBoundTerms][n_rounds]
+  uint32_t* lo_scale = bound + kBoundTerms * s.n_rounds;          // [n_rounds][n_ctiles]
+  ws += h.bound_bytes;
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += h.counter_bytes;
   int32_t* list = reinterpret_cast<int32_t*>(ws);
@@ -523,30 +732,30 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   const int cap = kTokensPerBlock * s.n_rounds;
   NearTieList lst{counts, list, cap, nullptr};
 
-  hipLaunchKernelGGL(hash_init_kernel, dim3(1), dim3(256), 0, stream, cmax, s.n_rounds, n_near_ties);
+  hipLaunchKernelGGL(hash_init_kernel, dim3(1), dim3(256), 0, stream, bound, s.n_rounds, n_near_ties);
   const dim3 pg(s.n_ctiles, s.n_rounds);
   const dim3 grid(n_regions);
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, cmax, s, buckets, lst);
+      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, lo_scale, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, cmax, s, buckets, lst);
+      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, lo_scale, s, buckets, lst);
     }
   } else {
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
+      hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_ctiles, frag, rt, cmax);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, cmax, s, buckets, lst);
+      hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     }
   }
   if (marks) (void)hipEventRecord(marks[1], stream);

@@ -77,6 +77,39 @@ def test_hash_zero_and_duplicate_vectors(nat):
     del torch
 
 
+@pytest.mark.parametrize("rot_scale", [2.0 ** -40, 1.0, 2.0 ** 40])
+def test_hash_wide_dynamic_range(nat, rot_scale):
+    """Features whose magnitudes span about 10^8 inside one 32-feature block and
+    rotations scaled far from 1: the per-block fp8 scales of x and the per-tile
+    scale of the rotation's low part must still give exact bucket ids."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    B, H, L, d, nb, r = 1, 2, 1500, 128, 256, 2
+    x = rng.standard_normal((B, H, L, d)) * np.exp(rng.standard_normal((B, H, L, d)) * 3.0)
+    qk32 = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    rot = (rng.standard_normal((r, d, nb // 2)) * rot_scale).astype(np.float32)
+    b, ties = nat.lsh_hash(qk32.cuda(), torch.from_numpy(rot).cuda(), nb, return_near_ties=True)
+    flips, total = compare_buckets(host(b), qk32.float().numpy().astype(np.float64), rot, nb)
+    _say(f"[hash-range] scale {rot_scale:g}: flips {flips}/{total}, re-decided {int(ties.item())}")
+    assert flips == 0   # float64 re-decisions make the ids exact, not only outside near-ties
+
+
+def test_hash_repeatable(nat):
+    """Repeated calls give the same ids and the same near-tie count (every
+    workgroup's near-tie list is complete before the fix-up reads it)."""
+    inp = W.custom_inputs(2, 4, 3000, 64, 64, 3, dtype="bf16", seed=5)
+    qk, _, rot = to_device(inp)
+    first, t0 = nat.lsh_hash(qk, rot, 64, return_near_ties=True)
+    first = host(first)
+    for _ in range(6):
+        b, t = nat.lsh_hash(qk, rot, 64, return_near_ties=True)
+        assert int(t.item()) == int(t0.item())
+        assert np.array_equal(host(b), first)
+    flips, total = compare_buckets(first, inp.qk.astype(np.float64), inp.rotations, 64)
+    assert flips == 0
+
+
 def test_hash_one_bucket(nat):
     import torch
 
