@@ -24,18 +24,20 @@
 //               over its window (chunks c-1 and c), written per position.
 //   stats       per position: Z (log2 domain, over rounds) and D.
 //   key pass    per round, per key chunk c: its keys are seen by the queries
-//               of chunks c and c+1; each wavefront owns 16 keys (K and V rows
-//               as MFMA B operands in registers), streams the 128 queries
-//               through LDS, and accumulates dv^T and dk^T (feature x key
-//               tiles) in registers; then adds them to the rows of its keys
-//               (round 0 writes them, with dout added to dv on self-fallback
-//               rows, so no separate initialisation pass is needed).
+//               of chunks c and c+1; each wavefront owns 16 keys, streams the
+//               128 queries through LDS, and accumulates dv^T and dk^T
+//               (feature x key tiles) in registers; then adds them to the rows
+//               of its keys (round 0 writes them, with dout added to dv on
+//               self-fallback rows, so no separate initialisation pass is
+//               needed).
 //   query pass  per round, per query chunk c: keys of chunks c-1 and c; each
 //               wavefront owns 16 queries and accumulates dq^T.
-// Within a round every position is one key of one key chunk and one query of
-// one query chunk, so each pass has a single writer per row; the passes and
-// rounds run one after another on the stream, so the read-add-write of the
-// float32 gradient rows never races.
+// float32 inputs run the two passes as separate kernels; bf16 inputs run both
+// in one kernel over runs of consecutive chunks (below), which gathers every
+// row once per round instead of three times.  Within a round every position
+// is one key of one key chunk and one query of one query chunk, so each row
+// has a single writing workgroup; rounds run one after another on the stream,
+// so the read-add-write of the float32 gradient rows never races.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -466,6 +468,16 @@ __device__ __forceinline__ f32x4 dot_tile16(const uint16_t* arow, const bf16x8 (
   return acc;
 }
 
+// As dot_tile16, with the B rows read from LDS too (fewer live registers).
+template <int D>
+__device__ __forceinline__ f32x4 dot_tile16_ll(const uint16_t* arow, const uint16_t* brow, int g) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag<D>(arow, kk, g), lds_frag<D>(brow, kk, g), acc, 0, 0, 0);
+  return acc;
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float (&x)[2][4]) {
   u32x4 p;
   p[0] = pack_bf16x2(x[0][0], x[0][1]);
@@ -553,141 +565,312 @@ __global__ __launch_bounds__(256) void bwd_z16_kernel(const uint16_t* __restrict
   if (g == 0) z2_rounds[static_cast<size_t>(seg) * L + qpos] = (mrun == -INFINITY) ? -INFINITY : mrun + log2f(lrun);
 }
 
+// ------------------------------------------------ fused bf16 backward ----
+// One workgroup of 8 wavefronts per run of kRunChunks consecutive chunks of
+// one (batch*head), for one round.  Step q brings chunk q's rows (qk, v, dout,
+// gathered through perm; the perm entries themselves one step earlier) into
+// LDS once, next to chunk q-1's qk and v, and does both halves of the work on
+// them.  Wavefronts 0-3 take the query role and 4-7 the key role for row slab
+// w % 4 (16 rows of a chunk):
+//   query role: queries of chunk q; dq over the keys of chunks q-1 and q (as
+//     the query pass above), added to the rows at the end of the step;
+//   key role: keys of chunk q-1, then of chunk q.  The queries of chunk q
+//     finish chunk q-1's dk and dv (its other queries, chunk q-1, came one
+//     step earlier), the rows are written, and the same registers start chunk
+//     q's (as the key pass above).
+// A run also reads the chunk before it (keys of its first
+// query chunk, no key-role output) and takes the chunk after it (key role
+// only, to finish its last chunk), so every gradient row of a round has one
+// writing workgroup.  Inside it a row's dq (step q) precedes its dk (step
+// q + 1) by two barriers: in round 0 the query role stores and the key role
+// adds.  Compared with the separate passes every row is read once per round
+// instead of three times.
+constexpr int kRunChunks = 8;
+
 template <int D>
-__global__ __launch_bounds__(256) void bwd_key16_kernel(const uint16_t* __restrict__ qk, const uint16_t* __restrict__ vv,
-                                                        const uint16_t* __restrict__ dout,
-                                                        const int32_t* __restrict__ perm_all, BwdShape s, int round,
-                                                        const float* __restrict__ z2, const float* __restrict__ dd,
-                                                        float* __restrict__ dqk, float* __restrict__ dv) {
-  __shared__ BwdTile16<D> sh;
-  constexpr int kP = BwdTile16<D>::kPitch;
-  const int c = blockIdx.x, bh = blockIdx.y;
+struct alignas(16) FusedLds {
+  static constexpr int kP = D + 16;   // bf16 per row, as BwdTile16
+  uint16_t qk[2][kBT * kP];           // chunk c in slot c & 1
+  uint16_t v[2][kBT * kP];
+  uint16_t dout[kBT * kP];            // the current query chunk
+  int pos[2][kBT];
+  float z2[kBT];                      // Z (log2 domain) and D of the current query chunk
+  float dd[kBT];
+};
+
+// One chunk's rows in flight in registers (loaded during a step, stored to LDS
+// after its closing barrier): one 16-byte piece of each matrix per thread.
+template <int D, int T>
+struct FusedPrefetch {
+  static constexpr int kThreads = T;
+  static constexpr int kPieces = kBT * (D / 8);
+  static constexpr int kPer = (kPieces + T - 1) / T;   // pieces per thread and matrix
+  u32x4 q[kPer], v[kPer], o[kPer];
+  int pos;
+  float z2, dd;
+  int prow[kPer];   // perm entries of this thread's rows for the chunk to be loaded next
+  int ppos;         // (threads < 64) perm entry of row threadIdx.x of that chunk
+};
+
+// perm entries that fused_load needs for chunk c, loaded one step ahead so the
+// row gathers do not wait on them.
+template <int D, class PF>
+__device__ __forceinline__ void fused_perm(PF& f, const int32_t* __restrict__ perm, int c) {
+#pragma unroll
+  for (int i = 0; i < PF::kPer; ++i) {
+    const int u = threadIdx.x + PF::kThreads * i;
+    if (u < PF::kPieces) f.prow[i] = perm[c * kBT + u / (D / 8)];
+  }
+  if (threadIdx.x < kBT) f.ppos = perm[c * kBT + threadIdx.x];
+}
+
+// Rows of the chunk whose perm entries fused_perm put in f.
+template <int D, class PF>
+__device__ __forceinline__ void fused_load(PF& f, const uint16_t* __restrict__ qk,
+                                           const uint16_t* __restrict__ vv, const uint16_t* __restrict__ dout,
+                                           const float* __restrict__ z2, const float* __restrict__ dd, size_t row0,
+                                           bool with_dout) {
+#pragma unroll
+  for (int i = 0; i < PF::kPer; ++i) {
+    const int u = threadIdx.x + PF::kThreads * i;
+    if (u < PF::kPieces) {
+      const size_t off = (row0 + f.prow[i]) * D + 8 * (u % (D / 8));
+      f.q[i] = *reinterpret_cast<const u32x4*>(qk + off);
+      f.v[i] = *reinterpret_cast<const u32x4*>(vv + off);
+      if (with_dout) f.o[i] = *reinterpret_cast<const u32x4*>(dout + off);
+    }
+  }
+  if (threadIdx.x < kBT) {
+    f.pos = f.ppos;
+    if (with_dout) {
+      f.z2 = z2[row0 + f.pos];
+      f.dd = dd[row0 + f.pos];
+    }
+  }
+}
+
+template <int D, class PF>
+__device__ __forceinline__ void fused_store(const PF& f, FusedLds<D>& sh, int c, bool with_dout) {
+  constexpr int kP = FusedLds<D>::kP;
+  const int slot = c & 1;
+#pragma unroll
+  for (int i = 0; i < PF::kPer; ++i) {
+    const int u = threadIdx.x + PF::kThreads * i;
+    if (u < PF::kPieces) {
+      const int row = u / (D / 8), pc = u % (D / 8);
+      *reinterpret_cast<u32x4*>(&sh.qk[slot][row * kP + 8 * pc]) = f.q[i];
+      *reinterpret_cast<u32x4*>(&sh.v[slot][row * kP + 8 * pc]) = f.v[i];
+      if (with_dout) *reinterpret_cast<u32x4*>(&sh.dout[row * kP + 8 * pc]) = f.o[i];
+    }
+  }
+  if (threadIdx.x < kBT) {
+    sh.pos[slot][threadIdx.x] = f.pos;
+    if (with_dout) {
+      sh.z2[threadIdx.x] = f.z2;
+      sh.dd[threadIdx.x] = f.dd;
+    }
+  }
+}
+
+constexpr int kFusedThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
+    const uint16_t* __restrict__ qk, const uint16_t* __restrict__ vv, const uint16_t* __restrict__ dout,
+    const int32_t* __restrict__ perm_all, BwdShape s, int round, const float* __restrict__ z2,
+    const float* __restrict__ dd, float* __restrict__ dqk, float* __restrict__ dv) {
+  __shared__ FusedLds<D> sh;
+  constexpr int kP = FusedLds<D>::kP;
+  constexpr int kFull = D / 16;            // 16-feature gradient tiles of a row
+  using PF = FusedPrefetch<D, kFusedThreads>;
+  const int bh = blockIdx.y;
   const int L = s.seq_len;
   const int32_t* perm = perm_all + (static_cast<size_t>(bh) * s.n_rounds + round) * L;
   const size_t row0 = static_cast<size_t>(bh) * L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int kslot = c * kBT + 16 * wave + c16;
-  const int kpos = perm[kslot];
-  bf16x8 kf[D / 32], vf[D / 32];
-  load_row_frags<D>(kf, qk, row0 + kpos, g);
-  load_row_frags<D>(vf, vv, row0 + kpos, g);
-  f32x4 dvt[D / 16], dkt[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    dvt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    dkt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const bool key_role = wave >= 4;
+  const int own = 16 * (wave & 3) + c16;   // this lane's row (query or key) inside a chunk
+  const int c0 = blockIdx.x * kRunChunks;
+  const int c1 = min(c0 + kRunChunks, s.n_chunks) - 1;
+  const int q_end = min(c1 + 1, s.n_chunks - 1);
+
+  PF pf;
+  if (c0 > 0) {
+    fused_perm<D, PF>(pf, perm, c0 - 1);
+    fused_load<D, PF>(pf, qk, vv, dout, z2, dd, row0, false);
+    fused_store<D, PF>(pf, sh, c0 - 1, false);
   }
-  const int h_end = (c + 1 < s.n_chunks) ? 2 : 1;
-  for (int h = 0; h < h_end; ++h) {
-    const int qc = c + h;
-    __syncthreads();
-    stage_rows16<D>(sh.a, qk, perm, qc, row0);
-    stage_rows16<D>(sh.b, dout, perm, qc, row0);
-    if (threadIdx.x < kBT) {
-      const int p = perm[qc * kBT + threadIdx.x];
-      sh.pos[threadIdx.x] = p;
-      sh.slot[threadIdx.x] = qc * kBT + threadIdx.x;
-      sh.z2[threadIdx.x] = z2[row0 + p];
-      sh.dd[threadIdx.x] = dd[row0 + p];
-    }
-    __syncthreads();
+  fused_perm<D, PF>(pf, perm, c0);
+  fused_load<D, PF>(pf, qk, vv, dout, z2, dd, row0, true);
+  fused_store<D, PF>(pf, sh, c0, true);
+  if (c0 < q_end) fused_perm<D, PF>(pf, perm, c0 + 1);
+  __syncthreads();
+
+  // acc_a: dq (query role) or dv (key role); acc_b: dk (key role); old_*: the
+  // rows' current values.
+  f32x4 acc_a[kFull], acc_b[kFull], old_a[kFull], old_b[kFull];
+#pragma unroll
+  for (int i = 0; i < kFull; ++i) {
+    acc_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    acc_b[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // Key role, one (key chunk kc, query chunk q) block: S and dP for 64 queries x
+  // this lane's key, then dv^T += dout^T P and dk^T += q^T dS.
+  auto key_block = [&](int kc, int q) {
+    const uint16_t* krow = &sh.qk[kc & 1][own * kP];
+    const uint16_t* vrow = &sh.v[kc & 1][own * kP];
+    const int kslot = kc * kBT + own;
+    const int kpos = sh.pos[kc & 1][own];
+    const uint16_t* qbase = sh.qk[q & 1];
 #pragma unroll
     for (int qp = 0; qp < 2; ++qp) {
       float pv[2][4], dsv[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int qt = 2 * qp + u;
-        const f32x4 sacc = dot_tile16<D>(&sh.a[(16 * qt + c16) * kP], kf, g);   // S[query 16qt+4g+j][key c16]
-        const f32x4 pacc = dot_tile16<D>(&sh.b[(16 * qt + c16) * kP], vf, g);   // dout_q . v_key
+        const f32x4 sacc = dot_tile16_ll<D>(&qbase[(16 * qt + c16) * kP], krow, g);     // S[query 16qt+4g+j][key c16]
+        const f32x4 pacc = dot_tile16_ll<D>(&sh.dout[(16 * qt + c16) * kP], vrow, g);   // dout_q . v_key
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qr = 16 * qt + 4 * g + j;
-          bool ok = sh.slot[qr] != kslot;
-          if (s.causal) ok = ok && kpos < sh.pos[qr];
+          bool ok = q * kBT + qr != kslot;
+          if (s.causal) ok = ok && kpos < sh.pos[q & 1][qr];
           const float zq = sh.z2[qr];
           const float p = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
           pv[u][j] = p;
           dsv[u][j] = p * (pacc[j] - sh.dd[qr]);
         }
       }
-      // dv^T += dout^T P and dk^T += q^T dS over these 32 queries.
       const bf16x8 bp = pack8(pv), bs = pack8(dsv);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        dvt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.b, 32 * qp, dt, g, c16), bp, dvt[dt], 0, 0, 0);
-        dkt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.a, 32 * qp, dt, g, c16), bs, dkt[dt], 0, 0, 0);
+      for (int i = 0; i < kFull; ++i) {
+        acc_a[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.dout, 32 * qp, i, g, c16), bp,
+                                                           acc_a[i], 0, 0, 0);
+        acc_b[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(qbase, 32 * qp, i, g, c16), bs,
+                                                           acc_b[i], 0, 0, 0);
       }
     }
-  }
-  store_key_grads<D, true>(dvt, dkt, row0, kpos, g, round, z2, dout, s.scale, dqk, dv);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_query16_kernel(const uint16_t* __restrict__ qk,
-                                                          const uint16_t* __restrict__ vv,
-                                                          const uint16_t* __restrict__ dout,
-                                                          const int32_t* __restrict__ perm_all, BwdShape s, int round,
-                                                          const float* __restrict__ z2, const float* __restrict__ dd,
-                                                          float* __restrict__ dqk) {
-  __shared__ BwdTile16<D> sh;
-  constexpr int kP = BwdTile16<D>::kPitch;
-  const int c = blockIdx.x, bh = blockIdx.y;
-  const int L = s.seq_len;
-  const int32_t* perm = perm_all + (static_cast<size_t>(bh) * s.n_rounds + round) * L;
-  const size_t row0 = static_cast<size_t>(bh) * L;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c16 = lane & 15, g = lane >> 4;
-  const int qslot = c * kBT + 16 * wave + c16;
-  const int qpos = perm[qslot];
-  const float zq = z2[row0 + qpos];
-  const float dq = dd[row0 + qpos];
-  bf16x8 qf[D / 32], of[D / 32];
-  load_row_frags<D>(qf, qk, row0 + qpos, g);
-  load_row_frags<D>(of, dout, row0 + qpos, g);
-  f32x4 dqt[D / 16];
+  };
+  // Key role: load the current dv and dk (in round 0 dk holds this round's dq)
+  // of chunk kc's rows.
+  auto key_prefetch = [&](int kc) {
+    const int kpos = sh.pos[kc & 1][own];
+    const float* dvr = dv + (row0 + kpos) * D;
+    const float* dkr = dqk + (row0 + kpos) * D;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) dqt[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
-    const int kc = c - 1 + h;
-    __syncthreads();
-    stage_rows16<D>(sh.a, qk, perm, kc, row0);
-    stage_rows16<D>(sh.b, vv, perm, kc, row0);
-    if (threadIdx.x < kBT) {
-      sh.pos[threadIdx.x] = perm[kc * kBT + threadIdx.x];
-      sh.slot[threadIdx.x] = kc * kBT + threadIdx.x;
+    for (int i = 0; i < kFull; ++i) {
+      const int f = 16 * (i) + 4 * g;
+      old_b[i] = *reinterpret_cast<const f32x4*>(dkr + f);
+      old_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (round != 0) old_a[i] = *reinterpret_cast<const f32x4*>(dvr + f);
     }
-    __syncthreads();
+  };
+  // Key role: chunk kc's dk and dv are complete; add them to the rows (dv
+  // starts from zero in round 0, plus dout on self-fallback rows) and clear.
+  // (Loading the current values before the block's MFMAs would hide the
+  // wait, but the registers it needs make the kernel spill.)
+  auto key_store = [&](int kc) {
+    const int kpos = sh.pos[kc & 1][own];
+    float* dvr = dv + (row0 + kpos) * D;
+    float* dkr = dqk + (row0 + kpos) * D;
+    const bool fallback = round == 0 && z2[row0 + kpos] == -INFINITY;
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      float dsv[2][4];
+    for (int i = 0; i < kFull; ++i) {
+      const int f = 16 * (i) + 4 * g;
+      f32x4 a = old_a[i], b = old_b[i];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int kt = 2 * kp + u;
-        const f32x4 sacc = dot_tile16<D>(&sh.a[(16 * kt + c16) * kP], qf, g);   // S^T[key 16kt+4g+j][query c16]
-        const f32x4 pacc = dot_tile16<D>(&sh.b[(16 * kt + c16) * kP], of, g);   // v_key . dout_q
+      for (int j = 0; j < 4; ++j) {
+        a[j] += acc_a[i][j];
+        b[j] = fmaf(acc_b[i][j], s.scale, b[j]);
+      }
+      if (fallback) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kr = 16 * kt + 4 * g + j;
-          bool ok = sh.slot[kr] != qslot;
-          if (s.causal) ok = ok && sh.pos[kr] < qpos;
-          const float p = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
-          dsv[u][j] = p * (pacc[j] - dq);
+        for (int j = 0; j < 4; ++j) a[j] += bf16_to_f32(dout[(row0 + kpos) * D + f + j]);
+      }
+      *reinterpret_cast<f32x4*>(dvr + f) = a;
+      *reinterpret_cast<f32x4*>(dkr + f) = b;
+      acc_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      acc_b[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  // Query role, chunk q: dq^T += k^T dS^T over the keys of chunks q-1 and q,
+  // then stored (round 0) or added to the rows.
+  auto query_chunk = [&](int q) {
+    const uint16_t* qrow = &sh.qk[q & 1][own * kP];
+    const uint16_t* orow = &sh.dout[own * kP];
+    const int qslot = q * kBT + own;
+    const int qpos = sh.pos[q & 1][own];
+    const float zq = sh.z2[own];
+    const float dq = sh.dd[own];
+    float* dqr = dqk + (row0 + qpos) * D;
+    for (int kc = (q > 0 ? q - 1 : q); kc <= q; ++kc) {
+      const uint16_t* kbase = sh.qk[kc & 1];
+      const uint16_t* vbase = sh.v[kc & 1];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        float dsv[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kt = 2 * kp + u;
+          const f32x4 sacc = dot_tile16_ll<D>(&kbase[(16 * kt + c16) * kP], qrow, g);   // S^T[key 16kt+4g+j][query c16]
+          const f32x4 pacc = dot_tile16_ll<D>(&vbase[(16 * kt + c16) * kP], orow, g);   // v_key . dout_q
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kr = 16 * kt + 4 * g + j;
+            bool ok = kc * kBT + kr != qslot;
+            if (s.causal) ok = ok && sh.pos[kc & 1][kr] < qpos;
+            const float p = (ok && zq != -INFINITY) ? exp2f(fmaf(sacc[j], s.scale_log2, -zq)) : 0.0f;
+            dsv[u][j] = p * (pacc[j] - dq);
+          }
         }
+        const bf16x8 bs = pack8(dsv);
+#pragma unroll
+        for (int i = 0; i < kFull; ++i)
+          acc_a[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(kbase, 32 * kp, i, g, c16), bs, acc_a[i],
+                                                             0, 0, 0);
       }
-      const bf16x8 bs = pack8(dsv);   // dS^T over these 32 keys
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        dqt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag_t<D>(sh.a, 32 * kp, dt, g, c16), bs, dqt[dt], 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < kFull; ++i) {
+      old_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (round != 0) old_a[i] = *reinterpret_cast<const f32x4*>(dqr + 16 * i + 4 * g);
+    }
+#pragma unroll
+    for (int i = 0; i < kFull; ++i) {
+      f32x4 a = old_a[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = fmaf(acc_a[i][j], s.scale, a[j]);
+      *reinterpret_cast<f32x4*>(dqr + 16 * i + 4 * g) = a;
+      acc_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+
+  for (int q = c0; q <= q_end; ++q) {
+    const bool more = q < q_end;
+    if (more) {
+      fused_load<D, PF>(pf, qk, vv, dout, z2, dd, row0, true);   // chunk q + 1
+      if (q + 2 <= q_end) fused_perm<D, PF>(pf, perm, q + 2);
+    }
+    if (!key_role) {
+      if (q <= c1) query_chunk(q);
+    } else {
+      if (q - 1 >= c0) {
+        key_block(q - 1, q);
+        key_prefetch(q - 1);
+        key_store(q - 1);
+      }
+      if (q <= c1) key_block(q, q);
+    }
+    __syncthreads();
+    if (more) fused_store<D, PF>(pf, sh, q + 1, true);
+    __syncthreads();
   }
-  float* dqr = dqk + (row0 + qpos) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(dqr + 16 * dt + 4 * g);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = fmaf(dqt[dt][j], s.scale, a[j]);
-    *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = a;
+  // The sequence's last chunk has no following query chunk.
+  if (key_role && c1 == s.n_chunks - 1) {
+    key_prefetch(c1);
+    key_store(c1);
   }
 }
 
@@ -710,10 +893,8 @@ hipError_t launch_bwd_typed(const void* qk, const void* v, const void* out, cons
                      out, dout, n_rows, s.seq_len, s.n_rounds, z2, dd);
   for (int r = 0; r < s.n_rounds; ++r) {
     if constexpr (BF16) {
-      hipLaunchKernelGGL(bwd_key16_kernel<D>, dim3(s.n_chunks, bh), dim3(256), 0, stream, q16, v16, o16, perm, s, r,
-                         z2, dd, dqk, dv);
-      hipLaunchKernelGGL(bwd_query16_kernel<D>, dim3(s.n_chunks, bh), dim3(256), 0, stream, q16, v16, o16, perm, s, r,
-                         z2, dd, dqk);
+      hipLaunchKernelGGL(bwd_fused16_kernel<D>, dim3((s.n_chunks + kRunChunks - 1) / kRunChunks, bh),
+                         dim3(kFusedThreads), 0, stream, q16, v16, o16, perm, s, r, z2, dd, dqk, dv);
     } else {
       hipLaunchKernelGGL((bwd_key_kernel<D, false>), dim3(s.n_chunks, bh), dim3(256), 0, stream, qk, v, dout, perm, s,
                          r, z2, dd, dqk, dv);

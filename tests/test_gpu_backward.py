@@ -25,6 +25,9 @@ def _say(msg):
     (512, 128, 3, 8, True, "f32"),
     (1024, 64, 2, 32, True, "bf16"),
     (384, 128, 2, 4, False, "bf16"),
+    (64, 64, 2, 4, True, "bf16"),         # one chunk: a single run with no neighbour
+    (1600, 128, 2, 16, True, "bf16"),     # 25 chunks: runs of 8, 8, 8 and a last run of one chunk
+    (576, 64, 3, 8, False, "bf16"),       # 9 chunks: a full run and a one-chunk run
 ])
 def test_backward_matches_oracle(nat, L, d, r, nb, causal, dtype):
     import torch
