@@ -414,11 +414,15 @@ def backward_bench(args):
     """Backward pass on the workload: perm from the library's hash and sort,
     out from its forward, dout iid normal; times reformer_lsh_attend_backward.
 
+    The forward runs as reformer_lsh_attend_lse, and the timed backward takes
+    its log normaliser (the way a training step uses them); the backward that
+    recomputes the normalisers is timed too and reported on stderr.
+
     Work per head-token and round (bf16 MFMA for bf16 inputs, float32 MFMA
-    for float32 inputs): the z pass recomputes
-    S over the 2m-key window (2 * 2m * d flops), the key pass S, dP, dV and dK
-    for the 2m queries that see a key (4 * 2 * 2m * d), the query pass S, dP
-    and dQ over the window (3 * 2 * 2m * d).
+    for float32 inputs): the key role S, dP, dV and dK for the 2m queries that
+    see a key (4 * 2 * 2m * d), the query role S, dP and dQ over the window
+    (3 * 2 * 2m * d); recomputing the normalisers adds S over the window
+    (2 * 2m * d).
     """
     import numpy as np
     import torch
@@ -440,14 +444,18 @@ def backward_bench(args):
         v = torch.from_numpy(inp.v).cuda()
     rot = torch.from_numpy(inp.rotations).cuda()
     perm, _ = nat.lsh_sort(nat.lsh_hash(qk, rot, w.n_buckets), w.n_buckets, inverse=False)
-    out = nat.attend(qk, v, perm, w.chunk_len, w.causal)
+    out, lse = nat.attend(qk, v, perm, w.chunk_len, w.causal, return_lse=True)
     g = np.random.default_rng(np.random.SeedSequence([20200104, 950 + w.index]))
     dout = torch.from_numpy(g.standard_normal(tuple(v.shape), dtype=np.float32)).to(v.dtype).cuda()
-    fn = lambda: nat.attend_backward(qk, v, perm, w.chunk_len, w.causal, out, dout)  # noqa: E731
+    fn = lambda: nat.attend_backward(qk, v, perm, w.chunk_len, w.causal, out, dout, lse=lse)  # noqa: E731
     ms = time_calls(fn, args.steps, args.warmup)
+    ms_recompute = time_calls(lambda: nat.attend_backward(qk, v, perm, w.chunk_len, w.causal, out, dout),
+                              args.steps, args.warmup)
+    print(f"[bench] backward with the forward's normaliser {ms:.3f} ms; recomputing it {ms_recompute:.3f} ms",
+          file=sys.stderr, flush=True)
     N = w.batch * w.heads * w.seq_len
     win = min(2 * w.chunk_len, w.seq_len)
-    flops = N * w.n_rounds * (1 + 4 + 3) * 2 * win * w.d_head
+    flops = N * w.n_rounds * (4 + 3) * 2 * win * w.d_head
     ach = flops / (ms / 1e3) / 1e12
     # bf16 inputs run every contraction on the bf16 MFMA, float32 inputs on the float32 MFMA
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -458,7 +466,7 @@ def backward_bench(args):
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded)",
         "config": {"workload": f"backward_{w.name}", "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "d_head": w.d_head, "n_buckets": w.n_buckets, "chunk_len": w.chunk_len, "n_rounds": w.n_rounds,
-                   "causal": w.causal},
+                   "causal": w.causal, "normaliser": "saved by the forward (lse)"},
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(ach / peak, 4), "kernel": "bwd_*_kernel (whole pass)", "traffic": None},
     }

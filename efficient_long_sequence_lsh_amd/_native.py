@@ -38,6 +38,7 @@ SIGNATURES = {
     "reformer_lsh_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]),
     "reformer_lsh_attend_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "reformer_lsh_attend": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
+    "reformer_lsh_attend_lse": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]),
     "reformer_lsh_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "reformer_lsh_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
     "reformer_lsh_attention_timed": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p, _i, _p]),
@@ -46,6 +47,8 @@ SIGNATURES = {
     "reformer_lsh_feed_forward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "reformer_lsh_feed_forward": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, _p]),
     "reformer_lsh_attend_backward": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
+    "reformer_lsh_attend_backward_lse": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz,
+                                              _p]),
 }
 
 TIMED_EVENTS = 7   # RLSH_TIMED_EVENTS
@@ -178,13 +181,23 @@ def combine(o_rounds: torch.Tensor, z_rounds: torch.Tensor, v: torch.Tensor) -> 
     return out
 
 
-def attend(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk_len: int, causal: bool) -> torch.Tensor:
+def attend(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk_len: int, causal: bool,
+           return_lse: bool = False):
+    """``out`` (input dtype, ``[B, H, L, d]``); with ``return_lse`` also the
+    float32 ``[B, H, L]`` log normaliser (``reformer_lsh_attend_lse``)."""
     _check_pair(qk, v)
     B, H, L, d = qk.shape
     r = perm.shape[2]
     nbytes = int(lib().reformer_lsh_attend_workspace_bytes(_dtype_code(qk), B, H, L, d, r, int(chunk_len)))
     ws = _ws(nbytes, qk.device)
     out = torch.empty_like(v)
+    if return_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=qk.device)
+        st = lib().reformer_lsh_attend_lse(_dev(qk, "qk"), _dev(v, "v"), _dtype_code(qk), _dev(perm, "perm"), B, H, L,
+                                           d, r, int(chunk_len), int(bool(causal)), out.data_ptr(), lse.data_ptr(),
+                                           ws.data_ptr(), nbytes, _stream())
+        _check(st, "reformer_lsh_attend_lse")
+        return out, lse
     st = lib().reformer_lsh_attend(_dev(qk, "qk"), _dev(v, "v"), _dtype_code(qk), _dev(perm, "perm"), B, H, L, d, r,
                                    int(chunk_len), int(bool(causal)), out.data_ptr(), ws.data_ptr(), nbytes, _stream())
     _check(st, "reformer_lsh_attend")
@@ -242,8 +255,9 @@ def local_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk_len
 
 
 def attend_backward(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk_len: int, causal: bool,
-                    out: torch.Tensor, dout: torch.Tensor):
-    """Gradients ``(dqk, dv)`` (float32 ``[B, H, L, d]``) of ``attend`` for a fixed sorted order."""
+                    out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor | None = None):
+    """Gradients ``(dqk, dv)`` (float32 ``[B, H, L, d]``) of ``attend`` for a fixed sorted order;
+    ``lse`` (the forward's, from ``attend(..., return_lse=True)``) skips the normaliser pass."""
     _check_pair(qk, v)
     _check_pair(out, dout)
     B, H, L, d = qk.shape
@@ -254,6 +268,15 @@ def attend_backward(qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, chunk
     ws = _ws(nbytes, qk.device)
     dqk = torch.empty((B, H, L, d), dtype=torch.float32, device=qk.device)
     dv = torch.empty_like(dqk)
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L):
+            raise ValueError("lse must be float32 [B, H, L]")
+        st = lib().reformer_lsh_attend_backward_lse(_dev(qk, "qk"), _dev(v, "v"), _dtype_code(qk), _dev(perm, "perm"),
+                                                    B, H, L, d, r, int(chunk_len), int(bool(causal)), _dev(out, "out"),
+                                                    _dev(dout, "dout"), _dev(lse, "lse"), dqk.data_ptr(),
+                                                    dv.data_ptr(), ws.data_ptr(), nbytes, _stream())
+        _check(st, "reformer_lsh_attend_backward_lse")
+        return dqk, dv
     st = lib().reformer_lsh_attend_backward(_dev(qk, "qk"), _dev(v, "v"), _dtype_code(qk), _dev(perm, "perm"), B, H, L,
                                             d, r, int(chunk_len), int(bool(causal)), _dev(out, "out"),
                                             _dev(dout, "dout"), dqk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,

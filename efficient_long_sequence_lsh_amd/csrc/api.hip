@@ -140,21 +140,22 @@ FullLayout full_layout(rlsh_dtype_t dtype, int batch, int heads, int seq_len, in
 // mark (optional): event recorded between the two kernels.
 hipError_t run_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int bh, int seq_len,
                       int d_head, int n_rounds, int chunk_len, int causal, void* out, const RoundLayout& rl,
-                      void* o_mem, void* z_mem, hipStream_t stream, hipEvent_t* mark = nullptr) {
+                      void* o_mem, void* z_mem, hipStream_t stream, hipEvent_t* mark = nullptr,
+                      float* lse = nullptr) {
   const bool bf16 = dtype == RLSH_BF16;
   hipError_t e;
   if (rl.compact) {
     uint16_t* o16 = static_cast<uint16_t*>(o_mem);
     float2* zk = static_cast<float2*>(z_mem);
     e = rlsh::launch_attend_combine_compact(qk, v, perm, bh, seq_len, d_head, n_rounds, causal != 0, o16, zk, out,
-                                            stream, mark);
+                                            lse, stream, mark);
   } else {
     float* o = static_cast<float*>(o_mem);
     float* z = static_cast<float*>(z_mem);
     e = rlsh::launch_chunk_attend(qk, v, bf16, perm, bh, seq_len, d_head, n_rounds, chunk_len, causal != 0, o, z,
                                   stream);
     if (e == hipSuccess && mark) e = hipEventRecord(*mark, stream);
-    if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, bh, seq_len, d_head, n_rounds, out, stream);
+    if (e == hipSuccess) e = rlsh::launch_combine(o, z, v, bf16, bh, seq_len, d_head, n_rounds, out, lse, stream);
   }
   return e;
 }
@@ -256,7 +257,7 @@ rlsh_status_t reformer_lsh_combine(const float* o_rounds, const float* z_rounds,
       (st = check_aligned(out, "out")) != RLSH_OK)
     return st;
   return hip_status(rlsh::launch_combine(o_rounds, z_rounds, v, dtype == RLSH_BF16, batch * heads, seq_len, d_head,
-                                         n_rounds, out, stream),
+                                         n_rounds, out, nullptr, stream),
                     "reformer_lsh_combine");
 }
 
@@ -267,9 +268,11 @@ size_t reformer_lsh_attend_workspace_bytes(rlsh_dtype_t dtype, int batch, int he
   return attend_ws(dtype, batch, heads, seq_len, d_head, n_rounds, chunk_len);
 }
 
-rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int batch,
-                                  int heads, int seq_len, int d_head, int n_rounds, int chunk_len, int causal,
-                                  void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+rlsh_status_t attend_impl(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int batch,
+                          int heads, int seq_len, int d_head, int n_rounds, int chunk_len, int causal, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream, const char* name) {
   rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len);
   if (st != RLSH_OK) return st;
   if ((st = check_dtype(dtype)) != RLSH_OK) return st;
@@ -284,8 +287,26 @@ rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dt
     return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "attend workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
   return hip_status(run_attend(qk, v, dtype, perm, batch * heads, seq_len, d_head, n_rounds, chunk_len, causal, out, rl,
-                               ws, ws + rl.o_bytes, stream),
-                    "reformer_lsh_attend");
+                               ws, ws + rl.o_bytes, stream, nullptr, lse),
+                    name);
+}
+
+}  // namespace
+
+rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int batch,
+                                  int heads, int seq_len, int d_head, int n_rounds, int chunk_len, int causal,
+                                  void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attend_impl(qk, v, dtype, perm, batch, heads, seq_len, d_head, n_rounds, chunk_len, causal, out, nullptr,
+                     workspace, workspace_bytes, stream, "reformer_lsh_attend");
+}
+
+rlsh_status_t reformer_lsh_attend_lse(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm,
+                                      int batch, int heads, int seq_len, int d_head, int n_rounds, int chunk_len,
+                                      int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (lse == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "lse must be non-null");
+  return attend_impl(qk, v, dtype, perm, batch, heads, seq_len, d_head, n_rounds, chunk_len, causal, out, lse,
+                     workspace, workspace_bytes, stream, "reformer_lsh_attend_lse");
 }
 
 size_t reformer_lsh_workspace_bytes(rlsh_dtype_t dtype, int batch, int heads, int seq_len, int d_head, int n_rounds,
@@ -399,10 +420,12 @@ size_t reformer_lsh_attend_backward_workspace_bytes(int batch, int heads, int se
   return rlsh::backward_scratch_bytes(batch * heads, seq_len, n_rounds);
 }
 
-rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm,
-                                           int batch, int heads, int seq_len, int d_head, int n_rounds,
-                                           int chunk_len, int causal, const void* out, const void* dout, float* dqk,
-                                           float* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+rlsh_status_t backward_impl(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm, int batch,
+                            int heads, int seq_len, int d_head, int n_rounds, int chunk_len, int causal,
+                            const void* out, const void* dout, const float* lse, float* dqk, float* dv,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream, const char* name) {
   rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, -1, chunk_len);
   if (st != RLSH_OK) return st;
   if ((st = check_dtype(dtype)) != RLSH_OK) return st;
@@ -419,8 +442,28 @@ rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_d
   if (workspace == nullptr || workspace_bytes < need)
     return fail(RLSH_ERR_WORKSPACE_TOO_SMALL, "backward workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   return hip_status(rlsh::launch_attend_backward(qk, v, dtype == RLSH_BF16, perm, batch * heads, seq_len, d_head,
-                                                 n_rounds, causal != 0, out, dout, dqk, dv, workspace, stream),
-                    "reformer_lsh_attend_backward");
+                                                 n_rounds, causal != 0, out, dout, lse, dqk, dv, workspace, stream),
+                    name);
+}
+
+}  // namespace
+
+rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_dtype_t dtype, const int32_t* perm,
+                                           int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                           int chunk_len, int causal, const void* out, const void* dout, float* dqk,
+                                           float* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(qk, v, dtype, perm, batch, heads, seq_len, d_head, n_rounds, chunk_len, causal, out, dout,
+                       nullptr, dqk, dv, workspace, workspace_bytes, stream, "reformer_lsh_attend_backward");
+}
+
+rlsh_status_t reformer_lsh_attend_backward_lse(const void* qk, const void* v, rlsh_dtype_t dtype,
+                                               const int32_t* perm, int batch, int heads, int seq_len, int d_head,
+                                               int n_rounds, int chunk_len, int causal, const void* out,
+                                               const void* dout, const float* lse, float* dqk, float* dv,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (lse == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "lse must be non-null");
+  return backward_impl(qk, v, dtype, perm, batch, heads, seq_len, d_head, n_rounds, chunk_len, causal, out, dout, lse,
+                       dqk, dv, workspace, workspace_bytes, stream, "reformer_lsh_attend_backward_lse");
 }
 
 rlsh_status_t check_ff_shape(int n_tokens, int d_model, int d_ff, int chunk_tokens) {

@@ -383,6 +383,7 @@ struct RoundSink {
   float2* zk;            // as o16
   const uint16_t* v;     // kSinkFinal: self fallback rows
   uint16_t* out;         // kSinkFinal: output [bh, L, d]
+  float* lse;            // kSinkFinal, optional: log of the combined normaliser per position
 };
 
 // One chunk: queries = rows of buffer `cur`, keys = rows of `prv` (previous
@@ -575,6 +576,7 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
       for (int rho = 0; rho < np; ++rho) zmax = fmaxf(zmax, zk_of(rho).x);
     }
     u32x2 res[D / 16];
+    float row_lse = -INFINITY;
     if (zmax == -INFINITY) {   // no round has a valid target: the token's own value
       const uint16_t* vp = out.v + (row0 + qpos) * D;
 #pragma unroll
@@ -622,7 +624,9 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
         res[dt][0] = pack_bf16x2(acc[dt][0] * rs, acc[dt][1] * rs);
         res[dt][1] = pack_bf16x2(acc[dt][2] * rs, acc[dt][3] * rs);
       }
+      row_lse = zmax + __logf(wsum);
     }
+    if (out.lse != nullptr && g == 0) out.lse[row0 + qpos] = row_lse;
     uint16_t* dst = out.out + (row0 + qpos) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<u32x2*>(dst + 16 * dt + 4 * g) = res[dt];
@@ -735,7 +739,7 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   const int n_seg = bh * n_rounds;
   if (bf16 && s.chunk == kKTile && seq_len % kKTile == 0) {
-    RoundSink out{o_rounds, z_rounds, nullptr, nullptr, nullptr, nullptr};
+    RoundSink out{o_rounds, z_rounds, nullptr, nullptr, nullptr, nullptr, nullptr};
     return d == 64 ? launch_fast64<64, kSinkF32>(qk, v, perm, bh, n_rounds, 0, s, out, stream)
                    : launch_fast64<128, kSinkF32>(qk, v, perm, bh, n_rounds, 0, s, out, stream);
   }
@@ -760,7 +764,7 @@ hipError_t launch_final(const void* qk, const void* v, const int32_t* perm, int 
 
 hipError_t launch_attend_combine_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len,
                                          int d, int n_rounds, bool causal, uint16_t* o16, float2* zk, void* out,
-                                         hipStream_t stream, hipEvent_t* mark) {
+                                         float* lse, hipStream_t stream, hipEvent_t* mark) {
   AttnShape s{};
   s.seq_len = seq_len;
   s.chunk = kKTile;
@@ -768,7 +772,7 @@ hipError_t launch_attend_combine_compact(const void* qk, const void* v, const in
   s.n_qt = seq_len / kKTile;
   s.causal = causal ? 1 : 0;
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-  RoundSink sink{nullptr, nullptr, o16, zk, static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out)};
+  RoundSink sink{nullptr, nullptr, o16, zk, static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse};
   hipError_t e = d == 64 ? launch_fast64<64, kSinkCompact>(qk, v, perm, bh, n_rounds - 1, 0, s, sink, stream)
                          : launch_fast64<128, kSinkCompact>(qk, v, perm, bh, n_rounds - 1, 0, s, sink, stream);
   if (e == hipSuccess && mark != nullptr) e = hipEventRecord(*mark, stream);

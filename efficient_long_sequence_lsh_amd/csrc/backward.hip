@@ -177,11 +177,13 @@ __global__ __launch_bounds__(256) void bwd_z_kernel(const void* __restrict__ qk,
 
 // -------------------------------------------------------------- stats ----
 // D/8 lanes per position (8 features each): Z (log2 domain) over rounds and
-// D = dout . out.
+// D = dout . out.  With the forward's log normaliser (lse, natural log) Z is
+// that value times log2(e) and the per-round values are not read.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void bwd_stats_kernel(const float* __restrict__ z2_rounds, const void* __restrict__ out,
-                                                        const void* __restrict__ dout, int n_rows, int seq_len,
-                                                        int n_rounds, float* __restrict__ z2, float* __restrict__ dd) {
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const float* __restrict__ z2_rounds, const float* __restrict__ lse,
+                                                        const void* __restrict__ out, const void* __restrict__ dout,
+                                                        int n_rows, int seq_len, int n_rounds, float* __restrict__ z2,
+                                                        float* __restrict__ dd) {
   constexpr int kT = D / 8;
   const int row = (blockIdx.x * blockDim.x + threadIdx.x) / kT;
   const int sub = threadIdx.x % kT;
@@ -208,6 +210,11 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const float* __restrict_
 #pragma unroll
   for (int off = 1; off < kT; off <<= 1) acc += __shfl_xor(acc, off, kT);
   if (!live || sub != 0) return;
+  dd[row] = acc;
+  if (lse != nullptr) {
+    z2[row] = lse[row] * kLog2e;   // -inf stays -inf
+    return;
+  }
   const int bh = row / seq_len, pos = row - bh * seq_len;
   const float* zr = z2_rounds + static_cast<size_t>(bh) * n_rounds * seq_len + pos;
   float m = -INFINITY;
@@ -219,7 +226,6 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const float* __restrict_
     zz = m + log2f(sum);
   }
   z2[row] = zz;
-  dd[row] = acc;
 }
 
 // Add (or, in round 0, write) the key-side gradients of one key: the lane
@@ -875,22 +881,24 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
 }
 
 template <int D, bool BF16>
-hipError_t launch_bwd_typed(const void* qk, const void* v, const void* out, const void* dout, const int32_t* perm,
-                            int bh, const BwdShape& s, float* z2_rounds, float* z2, float* dd, float* dqk, float* dv,
-                            hipStream_t stream) {
+hipError_t launch_bwd_typed(const void* qk, const void* v, const void* out, const void* dout, const float* lse,
+                            const int32_t* perm, int bh, const BwdShape& s, float* z2_rounds, float* z2, float* dd,
+                            float* dqk, float* dv, hipStream_t stream) {
   const uint16_t* q16 = static_cast<const uint16_t*>(qk);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const uint16_t* o16 = static_cast<const uint16_t*>(dout);
-  if constexpr (BF16)
-    hipLaunchKernelGGL(bwd_z16_kernel<D>, dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, q16, perm, s,
-                       z2_rounds);
-  else
-    hipLaunchKernelGGL((bwd_z_kernel<D, false>), dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, qk, perm, s,
-                       z2_rounds);
+  if (lse == nullptr) {   // per-round normalisers, recomputed
+    if constexpr (BF16)
+      hipLaunchKernelGGL(bwd_z16_kernel<D>, dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, q16, perm, s,
+                         z2_rounds);
+    else
+      hipLaunchKernelGGL((bwd_z_kernel<D, false>), dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, qk, perm,
+                         s, z2_rounds);
+  }
   const int n_rows = bh * s.seq_len;
   const int stats_threads = n_rows * (D / 8);
   hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3((stats_threads + 255) / 256), dim3(256), 0, stream, z2_rounds,
-                     out, dout, n_rows, s.seq_len, s.n_rounds, z2, dd);
+                     lse, out, dout, n_rows, s.seq_len, s.n_rounds, z2, dd);
   for (int r = 0; r < s.n_rounds; ++r) {
     if constexpr (BF16) {
       hipLaunchKernelGGL(bwd_fused16_kernel<D>, dim3((s.n_chunks + kRunChunks - 1) / kRunChunks, bh),
@@ -913,8 +921,8 @@ size_t backward_scratch_bytes(int bh, int seq_len, int n_rounds) {
 }
 
 hipError_t launch_attend_backward(const void* qk, const void* v, bool bf16, const int32_t* perm, int bh, int seq_len,
-                                  int d, int n_rounds, bool causal, const void* out, const void* dout, float* dqk,
-                                  float* dv, void* workspace, hipStream_t stream) {
+                                  int d, int n_rounds, bool causal, const void* out, const void* dout,
+                                  const float* lse, float* dqk, float* dv, void* workspace, hipStream_t stream) {
   BwdShape s{};
   s.seq_len = seq_len;
   s.n_rounds = n_rounds;
@@ -928,10 +936,10 @@ hipError_t launch_attend_backward(const void* qk, const void* v, bool bf16, cons
   float* z2 = reinterpret_cast<float*>(ws + align_up(n * n_rounds * sizeof(float), 256));
   float* dd = reinterpret_cast<float*>(ws + align_up(n * n_rounds * sizeof(float), 256) + align_up(n * sizeof(float), 256));
   if (d == 64)
-    return bf16 ? launch_bwd_typed<64, true>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream)
-                : launch_bwd_typed<64, false>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream);
-  return bf16 ? launch_bwd_typed<128, true>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream)
-              : launch_bwd_typed<128, false>(qk, v, out, dout, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream);
+    return bf16 ? launch_bwd_typed<64, true>(qk, v, out, dout, lse, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream)
+                : launch_bwd_typed<64, false>(qk, v, out, dout, lse, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream);
+  return bf16 ? launch_bwd_typed<128, true>(qk, v, out, dout, lse, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream)
+              : launch_bwd_typed<128, false>(qk, v, out, dout, lse, perm, bh, s, z2_rounds, z2, dd, dqk, dv, stream);
 }
 
 }  // namespace rlsh

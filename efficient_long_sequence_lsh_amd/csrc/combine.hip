@@ -25,7 +25,8 @@ namespace {
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const float* __restrict__ z,
                                                       const void* __restrict__ v_raw, int n_rows, int seq_len,
-                                                      int n_rounds, void* __restrict__ out_raw) {
+                                                      int n_rounds, void* __restrict__ out_raw,
+                                                      float* __restrict__ lse) {
   constexpr int kTpr = D / 4;                 // threads per row
   constexpr int kRowsPerBlock = 256 / kTpr;
   const int sub = threadIdx.x % kTpr;
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float zmax = -INFINITY;
     for (int r = 0; r < n_rounds; ++r) zmax = fmaxf(zmax, z[zrow + static_cast<size_t>(r) * seq_len]);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float row_lse = -INFINITY;
     if (zmax == -INFINITY) {
       if constexpr (BF16) {
         const uint16_t* vv = static_cast<const uint16_t*>(v_raw) + static_cast<size_t>(row) * D + 4 * sub;
@@ -63,7 +65,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const float inv = 1.0f / wsum;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] *= inv;
+      row_lse = zmax + logf(wsum);
     }
+    if (lse != nullptr && sub == 0) lse[row] = row_lse;
     if constexpr (BF16) {
       u32x2 packed;
       packed[0] = pack_bf16x2(acc[0], acc[1]);
@@ -77,25 +81,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 template <int D, bool BF16>
 hipError_t launch_typed(const float* o, const float* z, const void* v, int n_rows, int seq_len, int n_rounds,
-                        void* out, hipStream_t stream) {
+                        void* out, float* lse, hipStream_t stream) {
   constexpr int kRowsPerBlock = 256 / (D / 4);
   int blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   blocks = std::max(1, std::min(blocks, 256 * 32));
   hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(blocks), dim3(256), 0, stream, o, z, v, n_rows, seq_len, n_rounds,
-                     out);
+                     out, lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const void* v, bool bf16, int bh, int seq_len,
-                          int d, int n_rounds, void* out, hipStream_t stream) {
+                          int d, int n_rounds, void* out, float* lse, hipStream_t stream) {
   const int n_rows = bh * seq_len;
   if (d == 64)
-    return bf16 ? launch_typed<64, true>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream)
-                : launch_typed<64, false>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream);
-  return bf16 ? launch_typed<128, true>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream)
-              : launch_typed<128, false>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, stream);
+    return bf16 ? launch_typed<64, true>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, lse, stream)
+                : launch_typed<64, false>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, lse, stream);
+  return bf16 ? launch_typed<128, true>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, lse, stream)
+              : launch_typed<128, false>(o_rounds, z_rounds, v, n_rows, seq_len, n_rounds, out, lse, stream);
 }
 
 }  // namespace rlsh

@@ -56,8 +56,10 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
                                int bh, int seq_len, int d, int n_rounds, int chunk_len, bool causal,
                                float* o_rounds, float* z_rounds, hipStream_t stream);
 
+// lse (optional): per position, the log of the combined softmax normaliser
+// over every round's targets (-inf on self-fallback rows).
 hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const void* v, bool bf16,
-                          int bh, int seq_len, int d, int n_rounds, void* out, hipStream_t stream);
+                          int bh, int seq_len, int d, int n_rounds, void* out, float* lse, hipStream_t stream);
 
 // Compact per-round intermediates for the bf16 pipeline with 64-slot chunks:
 // o as float16 scaled by 2^-k per row, (z, k) as float pairs.  Rounds
@@ -66,7 +68,7 @@ hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const vo
 bool compact_rounds_supported(bool bf16, int seq_len, int chunk_len);
 hipError_t launch_attend_combine_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len,
                                          int d, int n_rounds, bool causal, uint16_t* o16, float2* zk, void* out,
-                                         hipStream_t stream, hipEvent_t* mark);
+                                         float* lse, hipStream_t stream, hipEvent_t* mark);
 
 // Local (sliding-chunk) attention over separate q, k, v; out in the input dtype.
 hipError_t launch_local_attend(const void* q, const void* k, const void* v, bool bf16, int bh, int seq_len, int d,
@@ -75,9 +77,11 @@ hipError_t launch_local_attend(const void* q, const void* k, const void* v, bool
 // Gradients of chunk attention + combine for a given sorted order (chunks of
 // 64 slots): dqk, dv float32 [bh, L, d]; workspace backward_scratch_bytes().
 size_t backward_scratch_bytes(int bh, int seq_len, int n_rounds);
+// lse (optional): the forward's per-position log normaliser; when given the
+// normaliser pass is skipped.
 hipError_t launch_attend_backward(const void* qk, const void* v, bool bf16, const int32_t* perm, int bh, int seq_len,
-                                  int d, int n_rounds, bool causal, const void* out, const void* dout, float* dqk,
-                                  float* dv, void* workspace, hipStream_t stream);
+                                  int d, int n_rounds, bool causal, const void* out, const void* dout,
+                                  const float* lse, float* dqk, float* dv, void* workspace, hipStream_t stream);
 
 // Position-wise feed-forward y = relu(x W1^T + b1) W2^T + b2 in chunks of
 // positions (bf16 x, weights and y; float32 biases); hidden holds one chunk's

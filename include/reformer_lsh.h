@@ -174,6 +174,19 @@ rlsh_status_t reformer_lsh_attend(const void* qk, const void* v, rlsh_dtype_t dt
                                   int d_head, int n_rounds, int chunk_len, int causal, void* out,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* reformer_lsh_attend that also writes lse: float32 [B, H, L], device memory,
+ * 4-byte aligned; lse_i = Z_i = logsumexp_r z_r(i) (natural log), the log of
+ * the combined softmax normaliser of position i over every round's targets,
+ * -inf on self-fallback rows.  It is what reformer_lsh_attend_backward_lse
+ * takes to skip recomputing the normalisers.  A null lse is
+ * RLSH_ERR_INVALID_ARGUMENT; everything else as reformer_lsh_attend.
+ */
+rlsh_status_t reformer_lsh_attend_lse(const void* qk, const void* v, rlsh_dtype_t dtype,
+                                      const int32_t* perm, int batch, int heads, int seq_len,
+                                      int d_head, int n_rounds, int chunk_len, int causal, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* ----------------------------------------------------------- attention ----
  * The whole forward pass: hash -> sort -> chunk attention -> combine and
  * un-sort, out [B, H, L, d] in dtype.  workspace: at least
@@ -235,6 +248,19 @@ rlsh_status_t reformer_lsh_attend_backward(const void* qk, const void* v, rlsh_d
                                            const void* out, const void* dout, float* dqk, float* dv,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
+
+/* reformer_lsh_attend_backward given the forward's lse (float32 [B, H, L], as
+ * written by reformer_lsh_attend_lse for the same inputs and perm): the
+ * per-round normaliser pass is skipped.  Same workspace size; a null lse is
+ * RLSH_ERR_INVALID_ARGUMENT; everything else as reformer_lsh_attend_backward.
+ */
+rlsh_status_t reformer_lsh_attend_backward_lse(const void* qk, const void* v, rlsh_dtype_t dtype,
+                                               const int32_t* perm, int batch, int heads,
+                                               int seq_len, int d_head, int n_rounds, int chunk_len,
+                                               int causal, const void* out, const void* dout,
+                                               const float* lse, float* dqk, float* dv,
+                                               void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
 
 /* -------------------------------------------------------- feed-forward ----
  * Position-wise feed-forward layer applied to chunk_tokens positions at a time

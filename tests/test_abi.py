@@ -138,3 +138,19 @@ def test_feed_forward_rejects_bad_arguments(lib):
     assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 128, 256, 0, FAKE, FAKE, 16, None) == 3          # workspace
     assert lib.reformer_lsh_feed_forward_workspace_bytes(1000, 128, 256, 64) == 64 * 256 * 2
     assert lib.reformer_lsh_feed_forward_workspace_bytes(1000, 128, 256, 0) >= 1000 * 256 * 2
+
+
+def test_normaliser_entry_points_reject_bad_arguments(lib):
+    # attend_lse: qk, v, dtype, perm, B, H, L, d, r, m, causal, out, lse, ws, wsb, stream
+    call = lib.reformer_lsh_attend_lse
+    assert call(FAKE, FAKE, 1, FAKE, 1, 1, 256, 64, 2, 64, 1, FAKE, None, FAKE, 1 << 30, None) == 1       # null lse
+    assert call(FAKE, FAKE, 1, FAKE, 1, 1, 256, 96, 2, 64, 1, FAKE, FAKE, FAKE, 1 << 30, None) == 2       # d_head 96
+    assert call(FAKE, FAKE, 1, FAKE, 1, 1, 256, 64, 2, 64, 1, FAKE, FAKE, FAKE, 16, None) == 3            # workspace
+    # backward_lse: qk, v, dtype, perm, B, H, L, d, r, m, causal, out, dout, lse, dqk, dv, ws, wsb, stream
+    call = lib.reformer_lsh_attend_backward_lse
+    assert call(FAKE, FAKE, 1, FAKE, 1, 1, 256, 64, 2, 64, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30,
+                None) == 1                                                                                # null lse
+    assert call(FAKE, FAKE, 1, FAKE, 1, 1, 256, 64, 2, 32, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                None) == 2                                                                                # 32-slot chunks
+    assert call(FAKE, FAKE, 1, FAKE, 1, 1, 256, 64, 2, 64, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                None) == 3                                                                                # workspace

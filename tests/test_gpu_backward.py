@@ -59,6 +59,50 @@ def test_backward_matches_oracle(nat, L, d, r, nb, causal, dtype):
         assert ex <= tol and ev <= tol
 
 
+@pytest.mark.parametrize("L,d,r,causal,dtype", [
+    (512, 64, 2, True, "f32"),
+    (1024, 128, 3, True, "bf16"),
+    (640, 64, 4, False, "bf16"),
+])
+def test_backward_with_forward_normaliser(nat, L, d, r, causal, dtype):
+    """attend(..., return_lse=True) gives the combined log normaliser; the
+    backward that takes it skips its own normaliser pass and gives the same
+    gradients (and the oracle's)."""
+    import torch
+
+    _say(f"[bwd-lse] L{L} d{d} r{r} causal={causal} {dtype}")
+    nb = 8
+    inp = W.custom_inputs(1, 2, L, d, nb, r, dtype=dtype, seed=L + 7 * r)
+    qk, v, rot = to_device(inp)
+    perm, _ = nat.lsh_sort(nat.lsh_hash(qk, rot, nb), nb)
+    out, lse = nat.attend(qk, v, perm, 64, causal, return_lse=True)
+    assert torch.equal(out, nat.attend(qk, v, perm, 64, causal))   # the same output with or without lse
+    g = np.random.default_rng(L + 3)
+    dout_h = g.standard_normal((1, 2, L, d)).astype(np.float32)
+    if dtype == "bf16":
+        dbits = W.f32_to_bf16_bits(dout_h)
+        dout_h = W.bf16_bits_to_f32(dbits)
+        dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        dout = torch.from_numpy(dout_h).cuda()
+    dqk0, dv0 = (host(t) for t in nat.attend_backward(qk, v, perm, 64, causal, out, dout))
+    dqk1, dv1 = (host(t) for t in nat.attend_backward(qk, v, perm, 64, causal, out, dout, lse=lse))
+    ph = host(perm)
+    for h in range(2):
+        _, wx, wv = oracle.lsh_attention_head_grad(inp.qk[0, h].astype(np.float64), inp.v[0, h].astype(np.float64),
+                                                   ph[0, h], 64, causal, dout_h[0, h].astype(np.float64))
+        scale = max(1.0, float(np.abs(wx).max()), float(np.abs(wv).max()))
+        tol = (1e-4 if dtype == "f32" else 2e-2) * scale
+        e_same = max(float(np.abs(dqk1[0, h] - dqk0[0, h]).max()), float(np.abs(dv1[0, h] - dv0[0, h]).max()))
+        ex, ev = float(np.abs(dqk1[0, h] - wx).max()), float(np.abs(dv1[0, h] - wv).max())
+        _say(f"  head {h}: lse vs recomputed {e_same:.2e}; vs oracle dqk {ex:.2e} dv {ev:.2e} (scale {scale:.2f})")
+        # bf16: P and dS are rounded to bf16 for the gradient contractions, so a
+        # normaliser that differs in its last float32 bits can move single
+        # roundings by one bf16 step (2^-8 relative)
+        assert e_same <= (1e-5 if dtype == "f32" else 4e-3) * scale
+        assert ex <= tol and ev <= tol
+
+
 def test_backward_rejects_other_chunk_lengths(nat):
     import torch
 

@@ -270,6 +270,39 @@ def test_attention_workloads(nat, name):
     assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("L,d,r,m,dtype,causal", [
+    (1024, 64, 2, 64, "f32", True),       # float32 rounds + combine kernel
+    (1024, 64, 3, 32, "bf16", False),     # bf16 with 32-slot chunks: float32 rounds + combine kernel
+    (2048, 128, 4, 64, "bf16", True),     # compact rounds, last round combines (three rows prefetched)
+    (1536, 64, 5, 64, "bf16", True),      # compact rounds, generic last-round combine
+])
+def test_attend_log_normaliser(nat, L, d, r, m, dtype, causal):
+    """lse = logsumexp over rounds of z_r: the log of the combined softmax
+    normaliser, -inf on self-fallback rows (checked against the oracle's z)."""
+    _say(f"[lse] L{L} d{d} r{r} m{m} {dtype} causal={causal}")
+    nb = 16
+    inp = W.custom_inputs(1, 2, L, d, nb, r, dtype=dtype, seed=L + r + m)
+    qk, v, rot = to_device(inp)
+    gb = nat.lsh_hash(qk, rot, nb)
+    perm, _ = nat.lsh_sort(gb, nb)
+    out, lse = nat.attend(qk, v, perm, m, causal, return_lse=True)
+    lse, gbh = host(lse), host(gb)
+    x, vv = inp.qk.astype(np.float64), inp.v.astype(np.float64)
+    worst = 0.0
+    for h in range(2):
+        z = oracle.lsh_attention_head(x[0, h], vv[0, h], inp.rotations, nb, m, causal, buckets=gbh[0, h])["z"]
+        zmax = z.max(axis=0)
+        fin = np.isfinite(zmax)
+        want = np.full(L, -np.inf)
+        want[fin] = zmax[fin] + np.log(np.exp(z[:, fin] - zmax[fin]).sum(axis=0))
+        got = lse[0, h]
+        assert np.array_equal(np.isfinite(got), fin)
+        err = np.abs(got[fin] - want[fin]) / np.maximum(1.0, np.abs(want[fin]))
+        worst = max(worst, float(err.max()) if err.size else 0.0)
+    _say(f"  max rel err {worst:.2e}")
+    assert worst <= 1e-5
+
+
 @pytest.mark.parametrize("L,d,r,causal", [
     (1024, 64, 1, True),      # one round: the combine reduces to normalisation and the self fallback
     (1536, 128, 3, False),    # round count without a specialised kernel, ragged run of chunks
