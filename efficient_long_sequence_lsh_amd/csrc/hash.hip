@@ -118,16 +118,25 @@ __device__ __forceinline__ float split_gap_bound(float xnorm, float xerr, float 
   return 2.0f * (xnorm * rho1 + xerr * rho2 + acc) * (1.0f + 1.0f / 1024.0f);
 }
 
-// Column-norm maxima per round, as float bits in [3][n_rounds]:
-// max_j |R_j|, max_j |R_j - R_hi,j - R_lo8,j|, max_j |R_lo8,j|.
+// Column-norm maxima, per rotation tile, as float bits in
+// [3][n_rounds][n_ctiles]: max_j |R_j|, max_j |R_j - R_hi,j - R_lo8,j|,
+// max_j |R_lo8,j| over the tile's columns j.  The set-up kernel writes one
+// entry per workgroup (no atomics, so no clearing pass); readers take the
+// maximum over a round's tiles.
 enum { kBoundCmax = 0, kBoundRes = 1, kBoundLo = 2, kBoundTerms = 3 };
 
-// ------------------------------------------------------ preparation ----
-// Zero the per-round column-norm maxima and the caller's near-tie total.
-__global__ void hash_init_kernel(uint32_t* bound_bits, int n_rounds, int32_t* n_near_ties) {
-  for (int t = threadIdx.x; t < kBoundTerms * n_rounds; t += blockDim.x) bound_bits[t] = 0u;
-  if (threadIdx.x == 0 && n_near_ties != nullptr) *n_near_ties = 0;
+// A round's maximum of one term; every lane of the wavefront must call it.
+__device__ __forceinline__ float round_bound(const uint32_t* __restrict__ bound_bits, int term, int n_rounds,
+                                             int n_ctiles, int round) {
+  const uint32_t* p = bound_bits + (static_cast<size_t>(term) * n_rounds + round) * n_ctiles;
+  uint32_t m = 0u;
+  for (int t = lane_id(); t < n_ctiles; t += 64) m = max(m, p[t]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, shfl_xor_u(m, off));
+  return __uint_as_float(m);
 }
+
+// ------------------------------------------------------ preparation ----
 
 // sqrt of a float64 sum of squares as float, rounded up (one float rounding,
 // at most 2^-24 relative, covered by the factor).
@@ -135,12 +144,12 @@ __device__ __forceinline__ uint32_t norm_bits_up(double sum) {
   return __float_as_uint(static_cast<float>(sqrt(sum)) * 1.0000005f);
 }
 
-// Largest value of each lane's group of 32 lanes into *dst (atomic max of
-// non-negative float bits).
+// Largest value of each lane's group of 32 lanes into *dst (non-negative
+// float bits).
 __device__ __forceinline__ void max32_to(uint32_t bits, uint32_t* dst) {
 #pragma unroll
   for (int off = 16; off > 0; off >>= 1) bits = max(bits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), off, 32)));
-  if ((threadIdx.x & 31) == 0) atomicMax(dst, bits);
+  if ((threadIdx.x & 31) == 0) *dst = bits;
 }
 
 // Fragment tile layout (16-byte units) for one (round, tile of 32 columns):
@@ -174,7 +183,7 @@ template <int D, bool FRAG>
 __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_rounds,
                                                            int n_ctiles, u32x4* __restrict__ frag,
                                                            float* __restrict__ rt, uint32_t* __restrict__ bound_bits,
-                                                           uint32_t* __restrict__ lo_scale) {
+                                                           uint32_t* __restrict__ lo_scale, int32_t* n_near_ties) {
   using FT = FragTile<D>;
   constexpr int kGroups = 8;               // k-ranges per column
   constexpr int kPerG = D / kGroups;       // 8 or 16 values
@@ -272,7 +281,11 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
     double sum = 0.0;
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) sum += part[i][threadIdx.x];
-    max32_to(c < half ? norm_bits_up(sum) : 0u, bound_bits + kBoundCmax * n_rounds + r);
+    const size_t slot = static_cast<size_t>(r) * n_ctiles + t;   // + term * n_rounds * n_ctiles
+    const size_t term = static_cast<size_t>(n_rounds) * n_ctiles;
+    max32_to(c < half ? norm_bits_up(sum) : 0u, bound_bits + kBoundCmax * term + slot);
+    // the caller's near-tie total starts from zero (the fix-up kernel adds to it)
+    if (threadIdx.x == 0 && t == 0 && r == 0 && n_near_ties != nullptr) *n_near_ties = 0;
     if (FRAG) {
       double sr = 0.0, sl = 0.0;
 #pragma unroll
@@ -280,8 +293,8 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
         sr += part_res[i][threadIdx.x];
         sl += part_lo[i][threadIdx.x];
       }
-      max32_to(norm_bits_up(sr), bound_bits + kBoundRes * n_rounds + r);
-      max32_to(norm_bits_up(sl), bound_bits + kBoundLo * n_rounds + r);
+      max32_to(norm_bits_up(sr), bound_bits + kBoundRes * term + slot);
+      max32_to(norm_bits_up(sl), bound_bits + kBoundLo * term + slot);
     }
   }
 }
@@ -475,9 +488,9 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
   auto round_end = [&](int n) {
     const int round = n / s.n_ctiles;
     if (n - round * s.n_ctiles != s.n_ctiles - 1) return;
-    const float cmax = __uint_as_float(bound_bits[kBoundCmax * s.n_rounds + round]);
-    const float rho1 = __uint_as_float(bound_bits[kBoundRes * s.n_rounds + round]);
-    const float rho2 = __uint_as_float(bound_bits[kBoundLo * s.n_rounds + round]);
+    const float cmax = round_bound(bound_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
+    const float rho1 = round_bound(bound_bits, kBoundRes, s.n_rounds, s.n_ctiles, round);
+    const float rho2 = round_bound(bound_bits, kBoundLo, s.n_rounds, s.n_ctiles, round);
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
       uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32);
@@ -565,9 +578,10 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
         top2_push(k1, k2, key);
       }
     }
+    const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
     if (live) {
       int c1 = static_cast<int>((k1 & code_mask) >> 1), c2 = static_cast<int>((k2 & code_mask) >> 1);
-      decide_and_store(k1, k2, c1, c2, kTauRel * xnorm * __uint_as_float(cmax_bits[kBoundCmax * s.n_rounds + round]),
+      decide_and_store(k1, k2, c1, c2, kTauRel * xnorm * cmax,
                        s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
@@ -699,7 +713,8 @@ HashScratch hash_scratch(const HashShape& s) {
   // per tile: bf16 R_hi (2 bytes) and fp8 R_lo (1 byte) for 32 columns x d
   h.frag_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * 32 * s.d * 3, 256);
   h.rt_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.half * s.d * sizeof(float), 256);
-  h.bound_bytes = align_up(static_cast<size_t>(s.n_rounds) * (kBoundTerms + s.n_ctiles) * sizeof(uint32_t), 256);
+  // per-tile column-norm maxima [kBoundTerms][n_rounds][n_ctiles], then fp8 scales [n_rounds][n_ctiles]
+  h.bound_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * (kBoundTerms + 1) * sizeof(uint32_t), 256);
   const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
   h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
   h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
@@ -722,8 +737,8 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   ws += h.frag_bytes;
   float* rt = reinterpret_cast<float*>(ws);
   ws += h.rt_bytes;
-  uint32_t* bound = reinterpret_cast<uint32_t*>(ws);               // [kBoundTerms][n_rounds]
-  uint32_t* lo_scale = bound + kBoundTerms * s.n_rounds;          // [n_rounds][n_ctiles]
+  uint32_t* bound = reinterpret_cast<uint32_t*>(ws);                          // [kBoundTerms][n_rounds][n_ctiles]
+  uint32_t* lo_scale = bound + static_cast<size_t>(kBoundTerms) * s.n_rounds * s.n_ctiles;   // [n_rounds][n_ctiles]
   ws += h.bound_bytes;
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += h.counter_bytes;
@@ -732,28 +747,27 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   const int cap = kTokensPerBlock * s.n_rounds;
   NearTieList lst{counts, list, cap, nullptr};
 
-  hipLaunchKernelGGL(hash_init_kernel, dim3(1), dim3(256), 0, stream, bound, s.n_rounds, n_near_ties);
   const dim3 pg(s.n_ctiles, s.n_rounds);
   const dim3 grid(n_regions);
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, lo_scale, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, lo_scale, s, buckets, lst);
     }
   } else {
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     }
