@@ -9,9 +9,10 @@
 // pass replaces a comparison sort.  A segment is cut into tiles.
 //   hist:    per-tile bucket counts with LDS atomics (order does not matter
 //            here), layout [segment][tile][bucket]
-//   scan:    one workgroup per segment: exclusive prefix over tiles per
-//            bucket (in place), then exclusive prefix over buckets of the
-//            bucket totals (the bucket bases)
+//   scan:    one thread per (segment, bucket): exclusive prefix over tiles
+//            (in place) and the bucket total; the exclusive prefix over
+//            buckets of the totals (the bucket bases) is formed by each
+//            scatter wavefront for its own segment
 //   scatter: one wavefront per tile walks it in position order, 64 keys at a
 //            time, with the keys of 32 groups loaded ahead.  Equal keys inside
 //            a group are found through a representative lane per key (LDS
@@ -36,7 +37,7 @@ namespace {
 
 constexpr int kHistThreads = 256;
 constexpr int kHistUnroll = 8;
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;
 constexpr int kScanBatch = 32;
 constexpr int kScatterBatch = 32;
 
@@ -85,52 +86,28 @@ __global__ __launch_bounds__(kHistThreads) void sort_hist_kernel(const int32_t* 
   for (int k = threadIdx.x; k < s.n_buckets; k += kHistThreads) out[k] = cnt[k];
 }
 
-// One workgroup per segment.  Thread i owns buckets [i*per, (i+1)*per):
-// exclusive prefix over tiles in place, bucket totals, then the exclusive
-// prefix over buckets (wave scans, then a scan of the 16 wave sums).
+// grid (n_seg, ceil(n_buckets / 256)): thread = one bucket of one segment.
+// Exclusive prefix of its count over tiles, in place, and its total.
 __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int32_t* __restrict__ counts, SortShape s,
-                                                                 int32_t* __restrict__ bucket_base) {
-  __shared__ int32_t wave_sum[kScanThreads / 64];
-  const int seg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (s.n_buckets + kScanThreads - 1) / kScanThreads;
-  const int k0 = min(s.n_buckets, tid * per), k1 = min(s.n_buckets, k0 + per);
-  int32_t* cseg = counts + static_cast<size_t>(seg) * s.n_tiles * s.n_buckets;
-  int32_t* bb = bucket_base + static_cast<size_t>(seg) * s.n_buckets;   // holds the totals first
-  int mine = 0;
-  for (int k = k0; k < k1; ++k) {
-    int32_t* c = cseg + k;
-    int run = 0;
-    for (int t0 = 0; t0 < s.n_tiles; t0 += kScanBatch) {
-      int v[kScanBatch];
+                                                                 int32_t* __restrict__ bucket_total) {
+  const int seg = blockIdx.x;
+  const int k = blockIdx.y * kScanThreads + threadIdx.x;
+  if (k >= s.n_buckets) return;
+  int32_t* c = counts + static_cast<size_t>(seg) * s.n_tiles * s.n_buckets + k;
+  int run = 0;
+  for (int t0 = 0; t0 < s.n_tiles; t0 += kScanBatch) {
+    int v[kScanBatch];
 #pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)   // unconditional loads (clamped index) stay in flight together
-        v[i] = c[static_cast<size_t>(min(t0 + i, s.n_tiles - 1)) * s.n_buckets];
+    for (int i = 0; i < kScanBatch; ++i)   // unconditional loads (clamped index) stay in flight together
+      v[i] = c[static_cast<size_t>(min(t0 + i, s.n_tiles - 1)) * s.n_buckets];
 #pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)
-        if (t0 + i < s.n_tiles) {
-          c[static_cast<size_t>(t0 + i) * s.n_buckets] = run;
-          run += v[i];
-        }
-    }
-    bb[k] = run;
-    mine += run;
+    for (int i = 0; i < kScanBatch; ++i)
+      if (t0 + i < s.n_tiles) {
+        c[static_cast<size_t>(t0 + i) * s.n_buckets] = run;
+        run += v[i];
+      }
   }
-  int inc = mine;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += o;
-  }
-  if (lane == 63) wave_sum[wave] = inc;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_sum[w];
-  int run = before + inc - mine;
-  for (int k = k0; k < k1; ++k) {
-    const int total = bb[k];
-    bb[k] = run;
-    run += total;
-  }
+  bucket_total[static_cast<size_t>(seg) * s.n_buckets + k] = run;
 }
 
 // LDS bytes of the scatter kernel: cur[n_buckets] (int32), then for the
@@ -165,7 +142,7 @@ __device__ __forceinline__ uint64_t group_peers(int key, bool act, int lane, int
 template <bool REPS>
 __global__ __launch_bounds__(64) void sort_scatter_kernel(const int32_t* __restrict__ buckets, SortShape s,
                                                           int per_xcd, const int32_t* __restrict__ tile_off,
-                                                          const int32_t* __restrict__ bucket_base,
+                                                          const int32_t* __restrict__ bucket_total,
                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   extern __shared__ __align__(16) unsigned char sort_lds[];
   int32_t* cur = reinterpret_cast<int32_t*>(sort_lds);
@@ -175,18 +152,42 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(const int32_t* __restr
   if (!tile_of_block(s, per_xcd, seg, t)) return;
   const int lane = threadIdx.x;
   const int32_t* off = tile_off + (static_cast<size_t>(seg) * s.n_tiles + t) * s.n_buckets;
-  const int32_t* bb = bucket_base + static_cast<size_t>(seg) * s.n_buckets;
-  for (int k0 = 0; k0 < s.n_buckets; k0 += 64 * 8) {
-    int b[8], o[8];
+  // Bucket bases of this segment (exclusive prefix of the totals over
+  // buckets): lane owns the contiguous buckets [lane*per, lane*per + per).
+  // cur[k] = base of k + this tile's offset in bucket k.
+  const int32_t* tot = bucket_total + static_cast<size_t>(seg) * s.n_buckets;
+  const int per = (s.n_buckets + 63) / 64;
+  const int k0 = min(s.n_buckets, lane * per), k1 = min(s.n_buckets, k0 + per);
+  int mine = 0;
+  for (int kb = k0; kb < k1; kb += 8) {
+    int v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {   // unconditional loads (clamped index) stay in flight together
-      const int k = min(k0 + 64 * i + lane, s.n_buckets - 1);
-      b[i] = bb[k];
+    for (int i = 0; i < 8; ++i) v[i] = tot[min(kb + i, s.n_buckets - 1)];   // in flight together
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (kb + i < k1) mine += v[i];
+  }
+  int inc = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  int run = inc - mine;
+  for (int kb = k0; kb < k1; kb += 8) {
+    int v[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = min(kb + i, s.n_buckets - 1);
+      v[i] = tot[k];
       o[i] = off[k];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (k0 + 64 * i + lane < s.n_buckets) cur[k0 + 64 * i + lane] = b[i] + o[i];
+      if (kb + i < k1) {
+        cur[kb + i] = run + o[i];
+        run += v[i];
+      }
   }
   if (REPS) mask[lane] = 0ull;
   __syncthreads();
@@ -270,21 +271,22 @@ hipError_t launch_sort(const int32_t* buckets, const SortShape& s, int32_t* perm
   }
   char* ws = static_cast<char*>(workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
-  int32_t* bases = reinterpret_cast<int32_t*>(
+  int32_t* totals = reinterpret_cast<int32_t*>(   // bucket totals [seg][bucket]
       ws + align_up(static_cast<size_t>(s.n_seg) * s.n_tiles * s.n_buckets * sizeof(int32_t), 256));
   const size_t lds = static_cast<size_t>(s.n_buckets) * sizeof(int32_t);
   const int n_blocks = s.n_seg * s.n_tiles;
   const int per_xcd = (n_blocks + 7) / 8;
   hipLaunchKernelGGL(sort_hist_kernel, dim3(8 * per_xcd), dim3(kHistThreads), lds, stream, buckets, s, per_xcd,
                      counts);
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(s.n_seg), dim3(kScanThreads), 0, stream, counts, s, bases);
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(s.n_seg, (s.n_buckets + kScanThreads - 1) / kScanThreads),
+                     dim3(kScanThreads), 0, stream, counts, s, totals);
   const size_t rep_lds = scatter_lds_bytes(s.n_buckets, true);
   if (rep_lds <= 65536)
     hipLaunchKernelGGL(sort_scatter_kernel<true>, dim3(8 * per_xcd), dim3(64), rep_lds, stream, buckets, s, per_xcd,
-                       counts, bases, perm, inv);
+                       counts, totals, perm, inv);
   else
     hipLaunchKernelGGL(sort_scatter_kernel<false>, dim3(8 * per_xcd), dim3(64), scatter_lds_bytes(s.n_buckets, false),
-                       stream, buckets, s, per_xcd, counts, bases, perm, inv);
+                       stream, buckets, s, per_xcd, counts, totals, perm, inv);
   return hipGetLastError();
 }
 
