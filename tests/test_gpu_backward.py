@@ -28,6 +28,7 @@ def _say(msg):
     (64, 64, 2, 4, True, "bf16"),         # one chunk: a single run with no neighbour
     (1600, 128, 2, 16, True, "bf16"),     # 25 chunks: runs of 8, 8, 8 and a last run of one chunk
     (576, 64, 3, 8, False, "bf16"),       # 9 chunks: a full run and a one-chunk run
+    (768, 64, 8, 32, True, "bf16"),       # eight rounds (the image-shaped configuration's round count)
 ])
 def test_backward_matches_oracle(nat, L, d, r, nb, causal, dtype):
     import torch
