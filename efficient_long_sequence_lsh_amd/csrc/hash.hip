@@ -17,10 +17,14 @@
 //     inputs use a plain FMA kernel.
 //   * The matrix product is computed transposed, D = R^T X^T, so that each lane
 //     receives 16 projections of ONE token per 32x32 tile.  Every projection is
-//     turned into an ordered 32-bit key: the float's magnitude bits shifted up
-//     by one, its sign in bit 0 and a candidate code in the low mantissa bits.
-//     A running top-two of keys per lane costs one med3 and one max per value;
-//     the two lanes sharing a token merge once per round.
+//     turned into an ordered 32-bit key with one and-or: the float's bits with
+//     the sign cleared and a candidate code in the low mantissa bits.  A
+//     running top-two of keys per lane takes a med3, a max and a max3 per two
+//     values.  The sign is left out of the keys: a running maximum of the raw
+//     float bits as signed integers (a max3 per two values) tells at the end
+//     of the round whether the winner is positive -- it is exactly when that
+//     maximum reaches the winner's magnitude.  The two lanes sharing a token
+//     merge once per round.
 //   * The top-two keys give the two leading candidates and their gap.  When the
 //     gap is below twice a bound on the error of one projection, the
 //     (position, round) is queued and a fix-up kernel re-decides it in float64
@@ -51,10 +55,27 @@ constexpr int kHashThreads = 256;           // 4 wavefronts
 constexpr int kStrips = 2;                  // 32-token strips per wavefront
 
 // --------------------------------------------------------------- keys ----
-// key = [magnitude bits 30..0 of the float, shifted up by one] [sign in bit 0],
-// with bits 1..code_bits replaced by a candidate code.  Unsigned order of keys
-// is the order of |p| truncated to (23 - code_bits) mantissa bits.
-__device__ __forceinline__ uint32_t rotl1(uint32_t b) { return __builtin_amdgcn_alignbit(b, b, 31); }
+// key = the float's bits with the sign cleared and bits 0..code_bits-1
+// replaced by a candidate code.  Unsigned order of keys is the order of |p|
+// truncated to (23 - code_bits) mantissa bits; codes make keys distinct.
+__device__ __forceinline__ uint32_t make_key(float p, uint32_t keep_mask, uint32_t code) {
+  return (__float_as_uint(p) & keep_mask) | code;
+}
+
+// v_med3_u32 written out, so that the compiler does not share its max(a, b)
+// with the max3 of the same values and then lose the max3.
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Top-two of {k1 >= k2, a, b}: the largest is max3(k1, a, b), the second
+// max(k2, med3(k1, a, b)).
+__device__ __forceinline__ void top2_push2(uint32_t& k1, uint32_t& k2, uint32_t a, uint32_t b) {
+  k2 = max(k2, med3_u32(k1, a, b));
+  k1 = max(max(k1, a), b);
+}
 
 __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
@@ -72,7 +93,7 @@ __device__ __forceinline__ void top2_merge(uint32_t& k1, uint32_t& k2, uint32_t 
 }
 
 __device__ __forceinline__ float key_magnitude(uint32_t key, uint32_t code_mask) {
-  return __uint_as_float(((key & ~code_mask) & ~1u) >> 1);
+  return __uint_as_float(key & ~code_mask);
 }
 
 // Queued (token, round) pairs live in one region per hash workgroup (capacity
@@ -96,15 +117,21 @@ __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int roun
 
 // Shared decision once a token's top-two keys and |x|_2 are known.
 // tau_x bounds the error of the gap between two projections before key
-// truncation, which is added here.
-__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int col1, int col2, float tau_x,
-                                                 int code_bits, int half, int tok, int seq_len,
+// truncation, which is added here.  smax is the largest raw projection bit
+// pattern as a signed integer (the largest positive projection, if any): the
+// winner is positive exactly when smax reaches its truncated magnitude.  Were
+// the winner negative while a positive projection reached that magnitude, the
+// two would share a truncated magnitude, so the gap would be zero and the
+// fix-up would decide.
+__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int32_t smax, int col1, int col2,
+                                                 float tau_x, int code_bits, int half, int tok, int seq_len,
                                                  int n_rounds, int round, int32_t* buckets, NearTieList lst) {
-  const uint32_t code_mask = ((1u << code_bits) - 1u) << 1;
+  const uint32_t code_mask = (1u << code_bits) - 1u;
   float m1 = key_magnitude(k1, code_mask);
   float m2 = key_magnitude(k2, code_mask);
   float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
-  int bucket = col1 + ((k1 & 1u) ? half : 0);
+  const bool positive = smax >= static_cast<int32_t>(k1 & ~code_mask);
+  int bucket = col1 + (positive ? 0 : half);
   int bh = tok / seq_len, pos = tok - bh * seq_len;
   buckets[(static_cast<size_t>(bh) * n_rounds + round) * seq_len + pos] = bucket;
   bool full = !(m1 > tau);
@@ -430,11 +457,12 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
   for (int i = threadIdx.x; i < kTileVec; i += kHashThreads) lds0[i] = frag[i];
   __syncthreads();
 
-  const uint32_t code_mask = ((1u << s.code_bits) - 1u) << 1;
-  const uint32_t keep_mask = ~code_mask;
+  const uint32_t code_mask = (1u << s.code_bits) - 1u;
+  const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
   uint32_t k1[kStrips], k2[kStrips];
+  int32_t smax[kStrips];
 #pragma unroll
-  for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; }
+  for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; smax[st] = INT32_MIN; }
 
   // Projections of tile n (lds buffer n & 1) into acc.
   auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur, int n) {
@@ -472,15 +500,18 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
     const uint32_t tile_code = (static_cast<uint32_t>(t) << 5) | (static_cast<uint32_t>(half_sel) << 4);
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
-      uint32_t a1 = (rotl1(__float_as_uint(acc[st][0])) & keep_mask) | (0u << 1);
-      uint32_t a2 = (rotl1(__float_as_uint(acc[st][1])) & keep_mask) | (1u << 1);
+      const uint32_t a1 = make_key(acc[st][0], keep_mask, 0u);
+      const uint32_t a2 = make_key(acc[st][1], keep_mask, 1u);
       uint32_t t1 = max(a1, a2), t2 = min(a1, a2);
+      int32_t sm = max(max(smax[st], __float_as_int(acc[st][0])), __float_as_int(acc[st][1]));
 #pragma unroll
-      for (int i = 2; i < 16; ++i) {
-        uint32_t key = (rotl1(__float_as_uint(acc[st][i])) & keep_mask) | (static_cast<uint32_t>(i) << 1);
-        top2_push(t1, t2, key);
+      for (int i = 2; i < 16; i += 2) {
+        top2_push2(t1, t2, make_key(acc[st][i], keep_mask, static_cast<uint32_t>(i)),
+                   make_key(acc[st][i + 1], keep_mask, static_cast<uint32_t>(i + 1)));
+        sm = max(max(sm, __float_as_int(acc[st][i])), __float_as_int(acc[st][i + 1]));
       }
-      top2_merge(k1[st], k2[st], t1 | (tile_code << 1), t2 | (tile_code << 1));
+      smax[st] = sm;
+      top2_merge(k1[st], k2[st], t1 | tile_code, t2 | tile_code);
     }
   };
   // After the last tile of a round: merge the two lanes that share each
@@ -495,18 +526,21 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
     for (int st = 0; st < kStrips; ++st) {
       uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32);
       top2_merge(k1[st], k2[st], o1, o2);
+      const int32_t sm = max(smax[st], static_cast<int32_t>(shfl_xor_u(static_cast<uint32_t>(smax[st]), 32)));
       int tok = tok_base + 32 * st + lane;
       if (lane < 32 && tok < s.n_tokens) {
-        uint32_t c1 = (k1[st] & code_mask) >> 1, c2 = (k2[st] & code_mask) >> 1;
+        uint32_t c1 = k1[st] & code_mask, c2 = k2[st] & code_mask;
         auto col_of = [](uint32_t c) {
           uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
           return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
         };
-        decide_and_store(k1[st], k2[st], col_of(c1), col_of(c2), split_gap_bound(xsq[st], xer[st], cmax, rho1, rho2),
-                         s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
+        decide_and_store(k1[st], k2[st], sm, col_of(c1), col_of(c2),
+                         split_gap_bound(xsq[st], xer[st], cmax, rho1, rho2), s.code_bits, s.half, tok, s.seq_len,
+                         s.n_rounds, round, buckets, lst);
       }
       k1[st] = 0u;
       k2[st] = 0u;
+      smax[st] = INT32_MIN;
     }
   };
   // Tile n + 1 straight into the idle LDS buffer (global_load_lds): each
@@ -559,10 +593,12 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
     sq = fmaf(x[k], x[k], sq);
   }
   const float xnorm = sqrtf(sq) * 1.0000005f;
-  const uint32_t code_mask = ((1u << s.code_bits) - 1u) << 1;
+  const uint32_t code_mask = (1u << s.code_bits) - 1u;
+  const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
   for (int round = 0; round < s.n_rounds; ++round) {
     const float* R = rot + static_cast<size_t>(round) * D * s.half;
     uint32_t k1 = 0u, k2 = 0u;
+    int32_t smax = INT32_MIN;
     for (int c0 = 0; c0 < s.half; c0 += kCols) {
       __syncthreads();
       for (int u = threadIdx.x; u < D * kCols; u += blockDim.x) {
@@ -574,14 +610,14 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
         float p = 0.0f;
 #pragma unroll
         for (int k = 0; k < D; ++k) p = fmaf(x[k], rt[k][j], p);
-        uint32_t key = (rotl1(__float_as_uint(p)) & ~code_mask) | (static_cast<uint32_t>(c0 + j) << 1);
-        top2_push(k1, k2, key);
+        top2_push(k1, k2, make_key(p, keep_mask, static_cast<uint32_t>(c0 + j)));
+        smax = max(smax, __float_as_int(p));
       }
     }
     const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
     if (live) {
-      int c1 = static_cast<int>((k1 & code_mask) >> 1), c2 = static_cast<int>((k2 & code_mask) >> 1);
-      decide_and_store(k1, k2, c1, c2, kTauRel * xnorm * cmax,
+      int c1 = static_cast<int>(k1 & code_mask), c2 = static_cast<int>(k2 & code_mask);
+      decide_and_store(k1, k2, smax, c1, c2, kTauRel * xnorm * cmax,
                        s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
