@@ -10,11 +10,11 @@
 //     bf16 inputs run on MFMA.  R = R_hi + R_lo with R_hi = bf16(R): the main
 //     term x.R_hi runs on v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products are
 //     exact in float32).  The correction x.R_lo, about 2^-9 of the result, runs
-//     on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in fp8 e4m3 and
-//     E8M0 block scales (a power of two per rotation tile for R_lo, one per
-//     32 features of a token for x), at half the cost of a bf16 pass.  Its
-//     error is bounded per token (below), so decisions stay exact.  Float32
-//     inputs use a plain FMA kernel.
+//     on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in fp6 e2m3 and
+//     an E8M0 scale per block of 32 features (of one rotation column, and of
+//     one token), at a quarter of the cost of a bf16 pass.  Its error is
+//     bounded per token (below), so decisions stay exact.  Float32 inputs use
+//     a plain FMA kernel.
 //   * The matrix product is computed transposed, D = R^T X^T, so that each lane
 //     receives 16 projections of ONE token per 32x32 tile.  Every projection is
 //     turned into an ordered 32-bit key with one and-or: the float's bits with
@@ -29,13 +29,13 @@
 //     gap is below twice a bound on the error of one projection, the
 //     (position, round) is queued and a fix-up kernel re-decides it in float64
 //     between those two candidates (or over all columns when even the leading
-//     magnitude is within the bound, e.g. x = 0).  By Cauchy-Schwarz, with x8
-//     and R_lo8 the fp8 operands, one projection is off by at most
-//       |x| max_j |R_j - R_hi,j - R_lo8,j| + |x - x8| max_j |R_lo8,j|
-//     plus float32 accumulation (below 2^-15 (|x| max_j |R_j| + |x8| max_j
-//     |R_lo8,j|) for up to 256 products), plus the key truncation.  The column
-//     maxima come from the set-up kernel, |x| and |x - x8| from the lane that
-//     converts x.
+//     magnitude is within the bound, e.g. x = 0).  By Cauchy-Schwarz, with x6
+//     and R_lo6 the fp6 operands, one projection is off by at most
+//       |x| max_j |R_j - R_hi,j - R_lo6,j| + |x - x6| max_j |R_lo6,j|
+//     plus float32 accumulation (below 2^-15 (|x| max_j |R_j| + |x6| max_j
+//     |R_lo6,j|) for up to 256 products), plus the key truncation.  The column
+//     maxima come from the set-up kernel, |x| and |x - x6| from the lanes that
+//     convert x.
 //   * Rotation fragments are pre-arranged in global memory in the exact order
 //     the MFMA A operands want them, so the copy into LDS is a straight
 //     coalesced memcpy and every wave reads 1 KB contiguous per fragment (no
@@ -146,8 +146,8 @@ __device__ __forceinline__ float split_gap_bound(float xnorm, float xerr, float 
 }
 
 // Column-norm maxima, per rotation tile, as float bits in
-// [3][n_rounds][n_ctiles]: max_j |R_j|, max_j |R_j - R_hi,j - R_lo8,j|,
-// max_j |R_lo8,j| over the tile's columns j.  The set-up kernel writes one
+// [3][n_rounds][n_ctiles]: max_j |R_j|, max_j |R_j - R_hi,j - R_lo6,j|,
+// max_j |R_lo6,j| over the tile's columns j.  The set-up kernel writes one
 // entry per workgroup (no atomics, so no clearing pass); readers take the
 // maximum over a round's tiles.
 enum { kBoundCmax = 0, kBoundRes = 1, kBoundLo = 2, kBoundTerms = 3 };
@@ -179,46 +179,80 @@ __device__ __forceinline__ void max32_to(uint32_t bits, uint32_t* dst) {
   if ((threadIdx.x & 31) == 0) *dst = bits;
 }
 
+// fp6 e2m3 (1 sign, 2 exponent bits with bias 1, 3 mantissa bits): the
+// magnitude codes 0..31 stand for c/8 below 2, 2 + (c-16)/4 below 4 and
+// 4 + (c-24)/2 up to 7.5; bit 5 is the sign.  Round to nearest, ties to the
+// even code, for |q| <= 7.5.
+__device__ __forceinline__ uint32_t e2m3_code(float q) {
+  const float m = fabsf(q);
+  float c;
+  if (m < 2.0f) c = rintf(m * 8.0f);
+  else if (m < 4.0f) c = 16.0f + rintf((m - 2.0f) * 4.0f);
+  else c = 24.0f + rintf((m - 4.0f) * 2.0f);
+  return static_cast<uint32_t>(c) | (q < 0.0f ? 32u : 0u);
+}
+
+__device__ __forceinline__ float e2m3_value(uint32_t code) {
+  const float c = static_cast<float>(code & 31u);
+  const float m = c < 16.0f ? c * 0.125f : (c < 24.0f ? 2.0f + (c - 16.0f) * 0.25f : 4.0f + (c - 24.0f) * 0.5f);
+  return (code & 32u) ? -m : m;
+}
+
+// Exponent E of the power of two that maps a block whose largest magnitude
+// is m into the e2m3 range (m * 2^-E in (3.75, 7.5]), kept inside E8M0's.
+__device__ __forceinline__ int e2m3_block_exp(float m) {
+  if (!(m > 0.0f)) return 0;
+  const int k = ilogbf(m);
+  const int e = m <= ldexpf(1.875f, k) ? k - 2 : k - 1;
+  return max(-127, min(e, 127));
+}
+
+// 32 codes packed as 6-bit fields, field e at bits 6e..6e+5 of six dwords.
+__device__ __forceinline__ void put_e2m3(uint32_t (&w)[6], int e, uint32_t code) {
+  const int bit = 6 * e;
+  w[bit / 32] |= code << (bit % 32);
+  if (bit % 32 > 26) w[bit / 32 + 1] |= code >> (32 - bit % 32);
+}
+
 // Fragment tile layout (16-byte units) for one (round, tile of 32 columns):
 //   [ks * 64 + l], ks < D/16: bf16 R_hi[k][c], c = 32t + l%32,
 //       k = 16ks + 8(l/32) + 0..7 (A operand of v_mfma_f32_32x32x16_bf16);
-//   [D * 4 + p * 64 + l], p = 2kb + j < D/32: fp8 R_lo[k][c] * 2^ea,
-//       k = 64kb + 32j + 16(l/32) + 0..15 (bytes 16j..16j+15 of the 32-byte A
-//       operand of the fp8 MFMA step kb).
-// The scaled MFMA pairs byte b of lane l with byte b of the B operand's lane
-// of the same l/32, and takes the E8M0 scale of bytes 16j..16j+15 (both lane
-// halves) from the lane 32j + row: so a block of 32 consecutive features
-// k = 64kb + 32j + 0..31 shares one scale.
+//   [D * 4 + (2kb + j) * 64 + l], kb < D/64, j = 0, 1: dwords 4j..4j+3 of the
+//       lane's 8-dword A operand of fp6 MFMA step kb: dwords 0..5 hold
+//       R_lo[k][c] * 2^-E, k = 64kb + 32(l/32) + e in 6-bit field e, dword 6
+//       the block's E8M0 scale byte 127 + E, dword 7 zero.
+// With fp6 operands the scaled MFMA pairs field e of lane l with field e of
+// the B operand's lane of the same l/32, and each lane's 32 fields form one
+// scale block whose scale that lane supplies.
 template <int D>
 struct FragTile {
   static constexpr int kHiSteps = D / 16;              // bf16 MFMA k-steps
-  static constexpr int kLoSteps = D / 64;              // fp8 MFMA k-steps
+  static constexpr int kLoSteps = D / 64;              // fp6 MFMA k-steps
   static constexpr int kHiVec = kHiSteps * 64;
   static constexpr int kVec = kHiVec + kLoSteps * 2 * 64;
 };
 
 // Per-call set-up, one workgroup per (tile of 32 rotation columns, round):
 //  - (FRAG) the fragment tile above, with R_hi = bf16(R) (round to nearest
-//    even), R_lo = R - R_hi (exact in float32) and ea the power of two that
-//    puts the tile's largest |R_lo| into [128, 256) (fp8 e4m3 tops out at
-//    448); the tile's E8M0 scale byte 127 - ea goes to lo_scale[round][tile];
+//    even), R_lo = R - R_hi (exact in float32) and a power of two 2^E per
+//    block of 32 features of a column that puts its largest |R_lo| into
+//    (3.75, 7.5];
 //  - R transposed to float32 [round][column][k], so that the fix-up reads a
 //    column as one contiguous row;
 //  - per-round maxima over columns of |R_j|, and (FRAG) of
-//    |R_j - R_hi,j - R_lo8,j| and |R_lo8,j| (float64 sums, rounded up).
+//    |R_j - R_hi,j - R_lo6,j| and |R_lo6,j| (float64 sums, rounded up).
 template <int D, bool FRAG>
 __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_rounds,
                                                            int n_ctiles, u32x4* __restrict__ frag,
                                                            float* __restrict__ rt, uint32_t* __restrict__ bound_bits,
-                                                           uint32_t* __restrict__ lo_scale, int32_t* n_near_ties) {
+                                                           int32_t* n_near_ties) {
   using FT = FragTile<D>;
   constexpr int kGroups = 8;               // k-ranges per column
   constexpr int kPerG = D / kGroups;       // 8 or 16 values
-  constexpr int kLoUnits = D / 16;         // 16-value k-ranges per column in the fp8 fragments
+  constexpr int kLoUnits = D / 32;         // fp6 scale blocks per column
   __shared__ double part[kGroups][32];
   __shared__ double part_res[kLoUnits][32];
   __shared__ double part_lo[kLoUnits][32];
-  __shared__ uint32_t lo_max_bits;
   __shared__ float tile_r[D][33];          // the tile's 32 columns (zero past half), one coalesced read
   const int t = blockIdx.x, r = blockIdx.y;
   const float* R = rot + static_cast<size_t>(r) * D * half;
@@ -232,20 +266,10 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < kPer; ++i) tile_r[threadIdx.x / 32 + 8 * i][cl] = v[i];
   }
-  if (threadIdx.x == 0) lo_max_bits = 0u;
   __syncthreads();
   auto rval = [&](int k, int cl) -> float { return tile_r[k][cl]; };
   auto lo_of = [](float v) -> float { return v - bf16_to_f32(f32_to_bf16_rne(v)); };
   if (FRAG) {
-    uint32_t m = 0u;
-    for (int u = threadIdx.x; u < D * 32; u += blockDim.x) m = max(m, __float_as_uint(fabsf(lo_of(rval(u / 32, u % 32)))));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, shfl_xor_u(m, off));
-    if ((threadIdx.x & 63) == 0) atomicMax(&lo_max_bits, m);
-    __syncthreads();
-    const uint32_t mb = lo_max_bits;
-    const int ea = mb == 0u ? 0 : min(134 - static_cast<int>(mb >> 23), 127);
-    if (threadIdx.x == 0) lo_scale[static_cast<size_t>(r) * n_ctiles + t] = static_cast<uint32_t>(127 - ea);
     u32x4* tile = frag + (static_cast<size_t>(r) * n_ctiles + t) * FT::kVec;
     for (int u = threadIdx.x; u < FT::kHiVec; u += blockDim.x) {
       const int ks = u / 64, l = u % 64;
@@ -258,34 +282,30 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
                     (static_cast<uint32_t>(f32_to_bf16_rne(rval(k0 + e + 1, c))) << 16);
       tile[u] = hi;
     }
-    for (int u = threadIdx.x; u < FT::kLoSteps * 128; u += blockDim.x) {
-      const int piece = u / 64, l = u % 64;
+    for (int u = threadIdx.x; u < FT::kLoSteps * 64; u += blockDim.x) {
+      const int kb = u / 64, l = u % 64;
       const int c = l & 31;
-      const int k0 = 32 * piece + 16 * (l >> 5);
-      u32x4 q;
+      const int k0 = 64 * kb + 32 * (l >> 5);
+      float m = 0.0f;
+#pragma unroll 8
+      for (int e = 0; e < 32; ++e) m = fmaxf(m, fabsf(lo_of(rval(k0 + e, c))));
+      const int E = e2m3_block_exp(m);
+      uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
       double s_res = 0.0, s_lo = 0.0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo[i] = lo_of(rval(k0 + 4 * e + i, c));
-        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(lo[0], ea), ldexpf(lo[1], ea), 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(lo[2], ea), ldexpf(lo[3], ea), w, true);
-        q[e] = w;
-        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-        const float dq[4] = {d01[0], d01[1], d23[0], d23[1]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const double lo8 = ldexp(static_cast<double>(dq[i]), -ea);
-          const double res = static_cast<double>(lo[i]) - lo8;
-          s_res += res * res;
-          s_lo += lo8 * lo8;
-        }
+#pragma unroll 8
+      for (int e = 0; e < 32; ++e) {
+        const float lo = lo_of(rval(k0 + e, c));
+        const uint32_t code = e2m3_code(ldexpf(lo, -E));
+        put_e2m3(w, e, code);
+        const double lo6 = ldexp(static_cast<double>(e2m3_value(code)), E);
+        const double res = static_cast<double>(lo) - lo6;
+        s_res += res * res;
+        s_lo += lo6 * lo6;
       }
-      tile[FT::kHiVec + u] = q;
-      part_res[2 * piece + (l >> 5)][l & 31] = s_res;
-      part_lo[2 * piece + (l >> 5)][l & 31] = s_lo;
+      tile[FT::kHiVec + (2 * kb) * 64 + l] = u32x4{w[0], w[1], w[2], w[3]};
+      tile[FT::kHiVec + (2 * kb + 1) * 64 + l] = u32x4{w[4], w[5], static_cast<uint32_t>(127 + E), 0u};
+      part_res[2 * kb + (l >> 5)][c] = s_res;
+      part_lo[2 * kb + (l >> 5)][c] = s_lo;
     }
   }
   const int cl = threadIdx.x & 31, g = threadIdx.x >> 5;
@@ -339,66 +359,88 @@ __device__ __forceinline__ void lds_dma16(const u32x4* g, u32x4* l) {
 // --------------------------------------------------- MFMA hash (bf16) ----
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// fp8 B operand of one token for fp8 MFMA step kb: this lane (half g = lane/32)
-// converts features k = 64kb + 32j + 16g + 0..15 (j = 0, 1) into bytes
-// 16j..16j+15.  Block j (features 64kb + 32j + 0..31, split over the two lanes
-// of the token) is scaled by 2^e_j, which puts its largest |x| into [128, 256);
-// the lane of half g returns block g's E8M0 scale byte.  Adds this lane's share
-// of |x - x8|^2 (exact differences: x has 8 significant bits, x8 is x rounded
-// to 4) to *err.
-template <int D>
-__device__ __forceinline__ i32x8 x_to_fp8(const uint16_t* __restrict__ xrow, bool live, int kb, int g, int* scale,
-                                          float* err) {
-  u32x4 raw[2][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      raw[j][h] = u32x4{0u, 0u, 0u, 0u};
-      if (live) raw[j][h] = *reinterpret_cast<const u32x4*>(xrow + 64 * kb + 32 * j + 16 * g + 8 * h);
-    }
-  int ej[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    uint32_t m = 0u;   // bf16 magnitudes order as integers
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m = max(m, max(raw[j][h][e] & 0x7fffu, (raw[j][h][e] >> 16) & 0x7fffu));
-    m = max(m, shfl_xor_u(m, 32));
-    ej[j] = m == 0u ? 0 : min(134 - static_cast<int>(m >> 7), 127);
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef float f32x32v __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// 32 values (element 2i from even[i], 2i+1 from odd[i]) divided by the power
+// of two `scale` and rounded to fp6 e2m3 codes, packed as 6-bit fields; and
+// back.  The conversions write their results while still reading their
+// sources, so the results are early-clobber outputs (never allocated over a
+// source).
+__device__ __forceinline__ u32x6 cvt_e2m3x32(f32x16v even, f32x16v odd, float scale) {
+  u32x6 r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3\n\ts_nop 4" : "=&v"(r) : "v"(even), "v"(odd), "v"(scale));
+  return r;
+}
+
+__device__ __forceinline__ f32x32v e2m3x32_to_f32(u32x6 p, float scale) {
+  f32x32v r;
+  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2\n\ts_nop 4" : "=&v"(r) : "v"(p), "v"(scale));
+  return r;
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 e2m3 A and B (formats 2, 2); the B
+// scale is byte `sel` of sb (sel is a constant once the caller's loops unroll).
+__device__ __forceinline__ f32x16 mfma_fp6(i32x8 a, i32x8 b, f32x16 c, int sa, int sb, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, sa, 3, sb);
   }
-  *scale = 127 - (g == 0 ? ej[0] : ej[1]);
-  i32x8 out;
+}
+
+// fp6 B operand of one token for fp6 MFMA step kb: this lane (half g =
+// lane/32) converts features k = 64kb + 32g + e, e = 0..31, into 6-bit field e,
+// scaled by 2^-E with E per this block of 32 (its E8M0 byte 127 + E goes to
+// *scale: each lane supplies its own block's scale).  Adds this lane's share
+// of |x - x6|^2 to *err (float32 sum of exact differences: x has 8
+// significant bits, x6 is x rounded to 4).
+template <int D>
+__device__ __forceinline__ i32x8 x_to_fp6(const uint16_t* __restrict__ xrow, bool live, int kb, int g, int* scale,
+                                          float* err) {
+  u32x4 raw[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    raw[h] = u32x4{0u, 0u, 0u, 0u};
+    if (live) raw[h] = *reinterpret_cast<const u32x4*>(xrow + 64 * kb + 32 * g + 8 * h);
+  }
+  uint32_t mb = 0u;   // bf16 magnitudes order as integers
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mb = max(mb, max(raw[h][e] & 0x7fffu, (raw[h][e] >> 16) & 0x7fffu));
+  // scales stay normal floats; a block below 2^-124 then rounds to zero codes
+  const int E = max(e2m3_block_exp(__uint_as_float(mb << 16)), -126);
+  *scale = 127 + E;
+  const float sc = ldexpf(1.0f, E);
+  f32x16v even, odd;
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      even[4 * h + e] = __uint_as_float(raw[h][e] << 16);
+      odd[4 * h + e] = __uint_as_float(raw[h][e] & 0xffff0000u);
+    }
+  const u32x6 w = cvt_e2m3x32(even, odd, sc);
+  const f32x32v back = e2m3x32_to_f32(w, sc);
   float acc = *err;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const float x0 = __uint_as_float(raw[j][h][e] << 16), x1 = __uint_as_float(raw[j][h][e] & 0xffff0000u);
-        const float x2 = __uint_as_float(raw[j][h][e + 1] << 16), x3 = __uint_as_float(raw[j][h][e + 1] & 0xffff0000u);
-        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x0, ej[j]), ldexpf(x1, ej[j]), 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x2, ej[j]), ldexpf(x3, ej[j]), w, true);
-        out[4 * j + 2 * h + e / 2] = static_cast<int>(w);
-        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-        const float r0 = x0 - ldexpf(d01[0], -ej[j]), r1 = x1 - ldexpf(d01[1], -ej[j]);
-        const float r2 = x2 - ldexpf(d23[0], -ej[j]), r3 = x3 - ldexpf(d23[1], -ej[j]);
-        acc = fmaf(r0, r0, acc);
-        acc = fmaf(r1, r1, acc);
-        acc = fmaf(r2, r2, acc);
-        acc = fmaf(r3, r3, acc);
-      }
+  for (int i = 0; i < 16; ++i) {
+    const float r0 = even[i] - back[2 * i], r1 = odd[i] - back[2 * i + 1];
+    acc = fmaf(r0, r0, acc);
+    acc = fmaf(r1, r1, acc);
+  }
   *err = acc;
-  return out;
+  return i32x8{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+               static_cast<int>(w[3]), static_cast<int>(w[4]), static_cast<int>(w[5]), 0, 0};
 }
 
 template <int D>
-__global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
+__global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kernel(
     const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ bound_bits,
-    const uint32_t* __restrict__ lo_scale, HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
+    HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
   using FT = FragTile<D>;
   constexpr int kSteps = FT::kHiSteps;
   constexpr int kLoSteps = FT::kLoSteps;
@@ -419,11 +461,14 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
   const int tok_base = (blockIdx.x * kWaves + wave) * (32 * kStrips);
 
   // B operands.  bf16: lane holds token (lane % 32), k = 16ks + 8*(lane/32) .. +7.
-  // fp8: see x_to_fp8.  |x| and |x - x8| per token, rounded up.
+  // fp6: see x_to_fp6.  |x| and |x - x6| per token, rounded up.
   bf16x8 xf[kStrips][kSteps];
-  i32x8 x8[kStrips][kLoSteps];
-  int xs8[kStrips][kLoSteps];
-  float xsq[kStrips], xer[kStrips];
+  i32x8 x6[kStrips][kLoSteps];
+  static_assert(kStrips * kLoSteps <= 4, "fp6 scale bytes share one register");
+  uint32_t xs6 = 0u;   // E8M0 byte of (st, kb) at byte st * kLoSteps + kb: the MFMA selects it
+  // |x| and |x - x6| per strip, needed once per round: kept in LDS (read back
+  // through a volatile pointer) rather than in registers the loop is short of.
+  __shared__ float2 xnorm[kStrips][kHashThreads];
 #pragma unroll
   for (int st = 0; st < kStrips; ++st) {
     const int tok = tok_base + 32 * st + (lane & 31);
@@ -444,12 +489,15 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
     }
     float err = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < kLoSteps; ++kb) x8[st][kb] = x_to_fp8<D>(xrow, live, kb, half_sel, &xs8[st][kb], &err);
+    for (int kb = 0; kb < kLoSteps; ++kb) {
+      int sc;
+      x6[st][kb] = x_to_fp6<D>(xrow, live, kb, half_sel, &sc, &err);
+      xs6 |= static_cast<uint32_t>(sc) << (8 * (st * kLoSteps + kb));
+    }
     acc += shfl_xor_f(acc, 32);
     err += shfl_xor_f(err, 32);
     // float32 sums of at most 256 squares: relative error below 2^-16
-    xsq[st] = sqrtf(acc) * (1.0f + 1.0f / 65536.0f);
-    xer[st] = sqrtf(err) * (1.0f + 1.0f / 65536.0f);
+    xnorm[st][threadIdx.x] = make_float2(sqrtf(acc) * (1.0f + 1.0f / 65536.0f), sqrtf(err) * (1.0f + 1.0f / 65536.0f));
   }
 
   const int n_total = s.n_rounds * s.n_ctiles;
@@ -466,7 +514,6 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
 
   // Projections of tile n (lds buffer n & 1) into acc.
   auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur, int n) {
-    const int sa = static_cast<int>(lo_scale[n]);
 #pragma unroll
     for (int st = 0; st < kStrips; ++st)
 #pragma unroll
@@ -478,12 +525,11 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
       const u32x4 p0 = cur[FT::kHiVec + (2 * kb) * 64 + lane];
       const u32x4 p1 = cur[FT::kHiVec + (2 * kb + 1) * 64 + lane];
       const i32x8 a_lo = {static_cast<int>(p0[0]), static_cast<int>(p0[1]), static_cast<int>(p0[2]),
-                          static_cast<int>(p0[3]), static_cast<int>(p1[0]), static_cast<int>(p1[1]),
-                          static_cast<int>(p1[2]), static_cast<int>(p1[3])};
+                          static_cast<int>(p0[3]), static_cast<int>(p1[0]), static_cast<int>(p1[1]), 0, 0};
+      const int sa = static_cast<int>(p1[2]);
 #pragma unroll
-      for (int st = 0; st < kStrips; ++st)
-        acc[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a_lo, x8[st][kb], acc[st], 0, 0, 0, sa, 0,
-                                                                  xs8[st][kb]);
+      for (int st = 0; st < kStrips; ++st)   // formats 2, 2: fp6 e2m3 A and B
+        acc[st] = mfma_fp6(a_lo, x6[st][kb], acc[st], sa, static_cast<int>(xs6), st * kLoSteps + kb);
     }
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
@@ -529,13 +575,15 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
       const int32_t sm = max(smax[st], static_cast<int32_t>(shfl_xor_u(static_cast<uint32_t>(smax[st]), 32)));
       int tok = tok_base + 32 * st + lane;
       if (lane < 32 && tok < s.n_tokens) {
+        const volatile float* xnv = reinterpret_cast<const volatile float*>(&xnorm[st][threadIdx.x]);
+        const float2 xn = make_float2(xnv[0], xnv[1]);
         uint32_t c1 = k1[st] & code_mask, c2 = k2[st] & code_mask;
         auto col_of = [](uint32_t c) {
           uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
           return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
         };
         decide_and_store(k1[st], k2[st], sm, col_of(c1), col_of(c2),
-                         split_gap_bound(xsq[st], xer[st], cmax, rho1, rho2), s.code_bits, s.half, tok, s.seq_len,
+                         split_gap_bound(xn.x, xn.y, cmax, rho1, rho2), s.code_bits, s.half, tok, s.seq_len,
                          s.n_rounds, round, buckets, lst);
       }
       k1[st] = 0u;
@@ -556,19 +604,39 @@ __global__ __launch_bounds__(kHashThreads, 3) void hash_mfma_kernel(
     }
   };
 
-  for (int n = 0; n < n_total; ++n) {
-    f32x16 acc[kStrips];
-    if ((n & 1) == 0) {
-      dma_next(lds1, n);
-      mfma_tile(acc, lds0, n);
-    } else {
-      dma_next(lds0, n);
-      mfma_tile(acc, lds1, n);
+  // Software pipeline: the MFMAs of tile n are issued between the vector
+  // instructions that turn tile n - 1's projections into keys (separate
+  // accumulators, no dependence), so one wavefront keeps the matrix core and
+  // the vector ALU busy at once.
+  f32x16 acc_a[kStrips], acc_b[kStrips];
+  auto step = [&](const u32x4* cur, u32x4* next, f32x16 (&acc)[kStrips], const f32x16 (&prev)[kStrips], int n) {
+    dma_next(next, n);
+    mfma_tile(acc, cur, n);
+    keys_tile(prev, n - 1);
+#pragma unroll
+    for (int i = 0; i < kStrips * (kSteps + kLoSteps); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then five vector instructions
     }
-    keys_tile(acc, n);
-    round_end(n);
+    round_end(n - 1);
     __syncthreads();   // also makes every wavefront's near-tie pushes visible to the count below
+  };
+  dma_next(lds1, 0);
+  mfma_tile(acc_a, lds0, 0);
+  __syncthreads();
+  int n = 1;
+  for (; n + 1 < n_total; n += 2) {
+    step(lds1, lds0, acc_b, acc_a, n);
+    step(lds0, lds1, acc_a, acc_b, n + 1);
   }
+  if (n < n_total) {   // n_total even: tile n (odd) is in lds1
+    step(lds1, lds0, acc_b, acc_a, n);
+    keys_tile(acc_b, n);
+  } else {
+    keys_tile(acc_a, n - 1);
+  }
+  round_end(n_total - 1);
+  __syncthreads();
   if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
 }
 
@@ -746,11 +814,11 @@ HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds
 
 HashScratch hash_scratch(const HashShape& s) {
   HashScratch h{};
-  // per tile: bf16 R_hi (2 bytes) and fp8 R_lo (1 byte) for 32 columns x d
+  // per tile: bf16 R_hi (2 bytes) and fp6 R_lo with its scales (1 byte) for 32 columns x d
   h.frag_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * 32 * s.d * 3, 256);
   h.rt_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.half * s.d * sizeof(float), 256);
-  // per-tile column-norm maxima [kBoundTerms][n_rounds][n_ctiles], then fp8 scales [n_rounds][n_ctiles]
-  h.bound_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * (kBoundTerms + 1) * sizeof(uint32_t), 256);
+  // per-tile column-norm maxima [kBoundTerms][n_rounds][n_ctiles]
+  h.bound_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_ctiles * kBoundTerms * sizeof(uint32_t), 256);
   const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
   h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
   h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
@@ -774,7 +842,6 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   float* rt = reinterpret_cast<float*>(ws);
   ws += h.rt_bytes;
   uint32_t* bound = reinterpret_cast<uint32_t*>(ws);                          // [kBoundTerms][n_rounds][n_ctiles]
-  uint32_t* lo_scale = bound + static_cast<size_t>(kBoundTerms) * s.n_rounds * s.n_ctiles;   // [n_rounds][n_ctiles]
   ws += h.bound_bytes;
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += h.counter_bytes;
@@ -788,22 +855,22 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, lo_scale, s, buckets, lst);
+      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, lo_scale, s, buckets, lst);
+      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
     }
   } else {
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, lo_scale, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     }

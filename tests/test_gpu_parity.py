@@ -110,6 +110,35 @@ def test_hash_repeatable(nat):
     assert flips == 0
 
 
+@pytest.mark.parametrize("d,dtype,all_pairs", [(64, "bf16", True), (128, "bf16", False), (64, "f32", True)])
+def test_hash_antipodal_columns(nat, d, dtype, all_pairs):
+    """Rotation columns in pairs R_2k+1 = -R_2k: the projections on a pair are
+    exact negatives, so +(xR)_2k and -(xR)_2k+1 (or the other two) tie exactly
+    and the lowest bucket must win.  With every column paired, each (position,
+    round) is a tie between a positive and a negative candidate of equal
+    magnitude and goes to the float64 re-decision; with half paired, ties and
+    clear winners of either sign mix."""
+    import torch
+
+    B, H, L, nb, r = 1, 2, 700, 128, 3
+    inp = W.custom_inputs(B, H, L, d, nb, r, dtype=dtype, seed=21 + d)
+    rot = inp.rotations.copy()
+    n_pairs = rot.shape[2] // 2 if all_pairs else rot.shape[2] // 4
+    rot[:, :, 1:2 * n_pairs:2] = -rot[:, :, 0:2 * n_pairs:2]
+    qk, _, _ = to_device(inp)
+    b, ties = nat.lsh_hash(qk, torch.from_numpy(rot).cuda(), nb, return_near_ties=True)
+    g = host(b)
+    x = inp.qk.astype(np.float64)
+    for h in range(H):
+        ob, _ = oracle.lsh_hash(x[0, h], rot, nb)
+        mism = g[0, h] != ob
+        assert not mism.any(), f"head {h}: gpu {g[0, h][mism][:8]} oracle {ob[mism][:8]}"
+    n_ties = int(ties.item())
+    _say(f"[hash-antipodal] d{d} {dtype} all_pairs={all_pairs}: re-decided {n_ties} of {B * H * L * r}")
+    if all_pairs:
+        assert n_ties == B * H * L * r
+
+
 def test_hash_one_bucket(nat):
     import torch
 
