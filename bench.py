@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
-MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA
+MFMA_FP6_PEAK_TFLOPS = 10100.0  # dense fp6 / fp4 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -229,9 +229,9 @@ def roofline_for(stage, ms, w):
         ach = work["flops"] / secs / 1e12
         rf = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
               "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-              # float32-accurate projections: x.R_hi on bf16 MFMA plus x.R_lo on fp8 MFMA,
+              # float32-accurate projections: x.R_hi on bf16 MFMA plus x.R_lo on fp6 MFMA,
               # each as many flops as the algorithm, priced at its own dense peak
-              "executed_mfma_frac": round(ach / MFMA_BF16_PEAK_TFLOPS + ach / MFMA_FP8_PEAK_TFLOPS, 4)}
+              "executed_mfma_frac": round(ach / MFMA_BF16_PEAK_TFLOPS + ach / MFMA_FP6_PEAK_TFLOPS, 4)}
     else:
         ach = work["bytes"] / secs / 1e9
         rf = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

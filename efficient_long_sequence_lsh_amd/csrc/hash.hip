@@ -282,30 +282,45 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
                     (static_cast<uint32_t>(f32_to_bf16_rne(rval(k0 + e + 1, c))) << 16);
       tile[u] = hi;
     }
-    for (int u = threadIdx.x; u < FT::kLoSteps * 64; u += blockDim.x) {
-      const int kb = u / 64, l = u % 64;
+    // Two threads per scale block (kb, lane l): thread p takes fields
+    // 16p..16p+15, which are exactly dwords 3p..3p+2 of the packed codes.
+    for (int u = threadIdx.x; u < FT::kLoSteps * 128; u += blockDim.x) {
+      const int blk = u >> 1, p = u & 1;
+      const int kb = blk / 64, l = blk % 64;
       const int c = l & 31;
-      const int k0 = 64 * kb + 32 * (l >> 5);
+      const int k0 = 64 * kb + 32 * (l >> 5) + 16 * p;
+      float lo[16];
       float m = 0.0f;
-#pragma unroll 8
-      for (int e = 0; e < 32; ++e) m = fmaxf(m, fabsf(lo_of(rval(k0 + e, c))));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        lo[e] = lo_of(rval(k0 + e, c));
+        m = fmaxf(m, fabsf(lo[e]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, 64));   // partner thread: u ^ 1, same wavefront
       const int E = e2m3_block_exp(m);
       uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
       double s_res = 0.0, s_lo = 0.0;
-#pragma unroll 8
-      for (int e = 0; e < 32; ++e) {
-        const float lo = lo_of(rval(k0 + e, c));
-        const uint32_t code = e2m3_code(ldexpf(lo, -E));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t code = e2m3_code(ldexpf(lo[e], -E));
         put_e2m3(w, e, code);
         const double lo6 = ldexp(static_cast<double>(e2m3_value(code)), E);
-        const double res = static_cast<double>(lo) - lo6;
+        const double res = static_cast<double>(lo[e]) - lo6;
         s_res += res * res;
         s_lo += lo6 * lo6;
       }
-      tile[FT::kHiVec + (2 * kb) * 64 + l] = u32x4{w[0], w[1], w[2], w[3]};
-      tile[FT::kHiVec + (2 * kb + 1) * 64 + l] = u32x4{w[4], w[5], static_cast<uint32_t>(127 + E), 0u};
-      part_res[2 * kb + (l >> 5)][c] = s_res;
-      part_lo[2 * kb + (l >> 5)][c] = s_lo;
+      // w[0..2] hold this thread's 16 fields (dwords 3p..3p+2 of the block)
+      const uint32_t first_of_partner = static_cast<uint32_t>(__shfl_xor(static_cast<int>(w[0]), 1, 64));
+      s_res += __shfl_xor(s_res, 1, 64);
+      s_lo += __shfl_xor(s_lo, 1, 64);
+      if (p == 0)
+        tile[FT::kHiVec + (2 * kb) * 64 + l] = u32x4{w[0], w[1], w[2], first_of_partner};
+      else
+        tile[FT::kHiVec + (2 * kb + 1) * 64 + l] = u32x4{w[1], w[2], static_cast<uint32_t>(127 + E), 0u};
+      if (p == 0) {
+        part_res[2 * kb + (l >> 5)][c] = s_res;
+        part_lo[2 * kb + (l >> 5)][c] = s_lo;
+      }
     }
   }
   const int cl = threadIdx.x & 31, g = threadIdx.x >> 5;
