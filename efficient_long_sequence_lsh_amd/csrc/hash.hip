@@ -628,6 +628,9 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
     dma_next(next, n);
     mfma_tile(acc, cur, n);
     keys_tile(prev, n - 1);
+    // every LDS read of the tile's A operands first, so that none waits
+    // behind the MFMAs; then one MFMA per five vector instructions
+    __builtin_amdgcn_sched_group_barrier(0x100, kSteps + 2 * kLoSteps, 0);
 #pragma unroll
     for (int i = 0; i < kStrips * (kSteps + kLoSteps); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
