@@ -587,10 +587,11 @@ __global__ __launch_bounds__(256) void bwd_z16_kernel(const uint16_t* __restrict
 // A run also reads the chunk before it (keys of its first
 // query chunk, no key-role output) and takes the chunk after it (key role
 // only, to finish its last chunk), so every gradient row of a round has one
-// writing workgroup.  Inside it a row's dq (step q) precedes its dk (step
-// q + 1) by two barriers: in round 0 the query role stores and the key role
-// adds.  Compared with the separate passes every row is read once per round
-// instead of three times.
+// writing workgroup.  A row's dq (step q) is finished one step before its dk
+// (step q + 1): the query role leaves dq in LDS and the key role adds it to
+// dk, so each row's dqk is read and written once per round (only written in
+// round 0).  Compared with the separate passes every row is read once per
+// round instead of three times.
 constexpr int kRunChunks = 8;
 
 template <int D>
@@ -602,6 +603,10 @@ struct alignas(16) FusedLds {
   int pos[2][kBT];
   float z2[kBT];                      // Z (log2 domain) and D of the current query chunk
   float dd[kBT];
+  // dq of query chunk c (scaled), slot c & 1, as the query-role lanes hold it:
+  // [wavefront][16-feature tile][lane]; the key-role lane of the same row
+  // (wavefront + 4, same lane) reads the same entries.
+  f32x4 dq[2][4][D / 16][64];
 };
 
 // One chunk's rows in flight in registers (loaded during a step, stored to LDS
@@ -759,8 +764,8 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
       }
     }
   };
-  // Key role: load the current dv and dk (in round 0 dk holds this round's dq)
-  // of chunk kc's rows.
+  // Key role: load the current dv and dqk of chunk kc's rows (nothing in
+  // round 0: both start from zero).
   auto key_prefetch = [&](int kc) {
     const int kpos = sh.pos[kc & 1][own];
     const float* dvr = dv + (row0 + kpos) * D;
@@ -768,13 +773,17 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
 #pragma unroll
     for (int i = 0; i < kFull; ++i) {
       const int f = 16 * (i) + 4 * g;
-      old_b[i] = *reinterpret_cast<const f32x4*>(dkr + f);
       old_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (round != 0) old_a[i] = *reinterpret_cast<const f32x4*>(dvr + f);
+      old_b[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (round != 0) {
+        old_a[i] = *reinterpret_cast<const f32x4*>(dvr + f);
+        old_b[i] = *reinterpret_cast<const f32x4*>(dkr + f);
+      }
     }
   };
-  // Key role: chunk kc's dk and dv are complete; add them to the rows (dv
-  // starts from zero in round 0, plus dout on self-fallback rows) and clear.
+  // Key role: chunk kc's dk and dv are complete; add them and chunk kc's dq
+  // (left in LDS by the query role) to the rows (plus dout to dv on
+  // self-fallback rows in round 0) and clear.
   // (Loading the current values before the block's MFMAs would hide the
   // wait, but the registers it needs make the kernel spill.)
   auto key_store = [&](int kc) {
@@ -786,10 +795,11 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
     for (int i = 0; i < kFull; ++i) {
       const int f = 16 * (i) + 4 * g;
       f32x4 a = old_a[i], b = old_b[i];
+      const f32x4 dqv = sh.dq[kc & 1][wave & 3][i][lane];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         a[j] += acc_a[i][j];
-        b[j] = fmaf(acc_b[i][j], s.scale, b[j]);
+        b[j] = fmaf(acc_b[i][j], s.scale, b[j] + dqv[j]);
       }
       if (fallback) {
 #pragma unroll
@@ -802,7 +812,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
     }
   };
   // Query role, chunk q: dq^T += k^T dS^T over the keys of chunks q-1 and q,
-  // then stored (round 0) or added to the rows.
+  // left in LDS for the key role, which adds it to the rows with dk.
   auto query_chunk = [&](int q) {
     const uint16_t* qrow = &sh.qk[q & 1][own * kP];
     const uint16_t* orow = &sh.dout[own * kP];
@@ -810,7 +820,6 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
     const int qpos = sh.pos[q & 1][own];
     const float zq = sh.z2[own];
     const float dq = sh.dd[own];
-    float* dqr = dqk + (row0 + qpos) * D;
     for (int kc = (q > 0 ? q - 1 : q); kc <= q; ++kc) {
       const uint16_t* kbase = sh.qk[kc & 1];
       const uint16_t* vbase = sh.v[kc & 1];
@@ -840,15 +849,10 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused16_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kFull; ++i) {
-      old_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (round != 0) old_a[i] = *reinterpret_cast<const f32x4*>(dqr + 16 * i + 4 * g);
-    }
+      f32x4 a;
 #pragma unroll
-    for (int i = 0; i < kFull; ++i) {
-      f32x4 a = old_a[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = fmaf(acc_a[i][j], s.scale, a[j]);
-      *reinterpret_cast<f32x4*>(dqr + 16 * i + 4 * g) = a;
+      for (int j = 0; j < 4; ++j) a[j] = acc_a[i][j] * s.scale;
+      sh.dq[q & 1][wave][i][lane] = a;
       acc_a[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
