@@ -44,6 +44,11 @@ def _device(arrs, bits):
     (320, 128, 320, 0, 0, True, "bf16"),     # one chunk: full causal attention
     (777, 64, 1000, 3, 3, False, "f32"),     # chunk_len > L
     (2048, 64, 128, 1, 1, True, "bf16"),
+    (2048, 128, 64, 1, 0, True, "bf16"),     # the 64K text setting's windows: two-slot key ring, two runs
+    (2112, 128, 64, 1, 1, False, "bf16"),    # three-slot ring at d = 128, a one-tile last run
+    (1280, 64, 64, 1, 0, True, "f32"),       # two-slot ring, float32
+    (1536, 128, 64, 1, 0, True, "f32"),      # two-slot ring, float32 at d = 128 (one workgroup per CU)
+    (2000, 64, 40, 1, 0, True, "bf16"),      # ring with chunks across tile edges, ragged last tile
 ])
 def test_local_attention_matches_oracle(nat, L, d, m, nb, na, causal, dtype):
     _say(f"[local] L{L} d{d} m{m} before{nb} after{na} causal={causal} {dtype}")
