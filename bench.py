@@ -401,7 +401,7 @@ def local_bench(args):
         "config": {"workload": f"local_{w.name}", "batch": B, "heads": H, "seq_len": L, "d_head": d, "chunk_len": m,
                    "n_before": nb, "n_after": na, "causal": w.causal},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "local_attend_kernel", "traffic": None},
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "local_ring_kernel", "traffic": None},
         "flops_per_token": 4 * window * d,
     }
     print(json.dumps(line), flush=True)
