@@ -138,11 +138,20 @@ __device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int32
   if (full || (m1 - m2) <= tau) push_near_tie(lst, tok, round, full, col1, col2);
 }
 
+// The float32 bounds assume that the products and partial sums that matter
+// stay far above the float32 subnormal range (and that the sums of squares
+// behind |x| do not underflow).  Below |x| = 2^-56 or max_j |R_j| = 2^-56
+// that is not assured, so such a (position, round) is re-decided in float64
+// over all columns (an infinite bound makes it a full re-decision).
+__device__ __forceinline__ float guard_tiny(float tau, float xnorm, float cmax) {
+  return (xnorm >= 0x1p-56f && cmax >= 0x1p-56f) ? tau : INFINITY;
+}
+
 // MFMA path: twice the per-projection bound (see the top of this file), with
 // a 2^-10 margin for the float32 evaluation of the bound itself.
 __device__ __forceinline__ float split_gap_bound(float xnorm, float xerr, float cmax, float rho1, float rho2) {
   const float acc = kAccRel * (xnorm * cmax + (xnorm + xerr) * rho2);
-  return 2.0f * (xnorm * rho1 + xerr * rho2 + acc) * (1.0f + 1.0f / 1024.0f);
+  return guard_tiny(2.0f * (xnorm * rho1 + xerr * rho2 + acc) * (1.0f + 1.0f / 1024.0f), xnorm, cmax);
 }
 
 // Column-norm maxima, per rotation tile, as float bits in
@@ -703,7 +712,7 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
     const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
     if (live) {
       int c1 = static_cast<int>(k1 & code_mask), c2 = static_cast<int>(k2 & code_mask);
-      decide_and_store(k1, k2, smax, c1, c2, kTauRel * xnorm * cmax,
+      decide_and_store(k1, k2, smax, c1, c2, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
                        s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }

@@ -139,6 +139,43 @@ def test_hash_antipodal_columns(nat, d, dtype, all_pairs):
         assert n_ties == B * H * L * r
 
 
+@pytest.mark.parametrize("x_exp,rot_exp,dtype", [
+    (-100, 0, "bf16"),    # |x| far below 2^-56: every decision in float64
+    (-128, 0, "bf16"),    # bf16 subnormal features
+    (-140, 0, "f32"),     # float32 subnormal features
+    (0, -70, "bf16"),     # tiny rotations
+    (60, 0, "bf16"),      # large features, ordinary path
+])
+def test_hash_extreme_scales(nat, x_exp, rot_exp, dtype):
+    """Features or rotations scaled by powers of two far from 1.  Where the
+    float32 error bounds would rest on subnormal arithmetic the kernel hands
+    the decision to the float64 re-decision, so ids match the oracle exactly."""
+    import torch
+
+    B, H, L, d, nb, r = 1, 2, 640, 64, 64, 2
+    inp = W.custom_inputs(B, H, L, d, nb, r, dtype="f32", seed=31 + abs(x_exp) + abs(rot_exp))
+    x = np.ldexp(inp.qk.astype(np.float64), x_exp)
+    rot = np.ldexp(inp.rotations.astype(np.float64), rot_exp).astype(np.float32)
+    if dtype == "bf16":
+        bits = W.f32_to_bf16_bits(x.astype(np.float32))
+        qk = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        x = W.bf16_bits_to_f32(bits).astype(np.float64)
+    else:
+        x32 = x.astype(np.float32)
+        qk = torch.from_numpy(x32).cuda()
+        x = x32.astype(np.float64)
+    b, ties = nat.lsh_hash(qk, torch.from_numpy(rot).cuda(), nb, return_near_ties=True)
+    g = host(b)
+    for h in range(H):
+        ob, _ = oracle.lsh_hash(x[0, h], rot, nb)
+        mism = g[0, h] != ob
+        assert not mism.any(), f"head {h}: gpu {g[0, h][mism][:8]} oracle {ob[mism][:8]}"
+    n_ties = int(ties.item())
+    _say(f"[hash-scale] x 2^{x_exp} R 2^{rot_exp} {dtype}: re-decided {n_ties} of {B * H * L * r}")
+    if x_exp <= -100 or rot_exp <= -70:
+        assert n_ties == B * H * L * r
+
+
 def test_hash_one_bucket(nat):
     import torch
 
