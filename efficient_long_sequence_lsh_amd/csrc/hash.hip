@@ -475,9 +475,24 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   __shared__ u32x4 lds0[kTileVec];   // two separate buffers, so that the compiler can tell
   __shared__ u32x4 lds1[kTileVec];   // the copy into one from the reads of the other
   __shared__ int ntie;
+  // Per-round maxima of the bound terms (float bits), gathered once here so
+  // that the end of a round reads them from LDS instead of waiting on global
+  // loads; with more rounds than fit, each round end reduces them itself.
+  constexpr int kLdsRounds = 64;
+  __shared__ uint32_t rbound[kLdsRounds][kBoundTerms];
+  const bool rb_lds = s.n_rounds <= kLdsRounds;
   static_assert(kWaves * 32 * kStrips == kTokensPerBlock, "near-tie regions assume 256 tokens per block");
   if (threadIdx.x == 0) ntie = 0;
   lst.lds_count = &ntie;
+  if (rb_lds) {
+    for (int i = threadIdx.x; i < s.n_rounds * kBoundTerms; i += kHashThreads) (&rbound[0][0])[i] = 0u;
+    __syncthreads();
+    const int per_term = s.n_rounds * s.n_ctiles;
+    for (int u = threadIdx.x; u < kBoundTerms * per_term; u += kHashThreads) {
+      const int term = u / per_term, round = (u - term * per_term) / s.n_ctiles;
+      atomicMax(&rbound[round][term], bound_bits[u]);   // non-negative float bits order as integers
+    }
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -589,9 +604,16 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   auto round_end = [&](int n) {
     const int round = n / s.n_ctiles;
     if (n - round * s.n_ctiles != s.n_ctiles - 1) return;
-    const float cmax = round_bound(bound_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
-    const float rho1 = round_bound(bound_bits, kBoundRes, s.n_rounds, s.n_ctiles, round);
-    const float rho2 = round_bound(bound_bits, kBoundLo, s.n_rounds, s.n_ctiles, round);
+    float cmax, rho1, rho2;
+    if (rb_lds) {
+      cmax = __uint_as_float(rbound[round][kBoundCmax]);
+      rho1 = __uint_as_float(rbound[round][kBoundRes]);
+      rho2 = __uint_as_float(rbound[round][kBoundLo]);
+    } else {
+      cmax = round_bound(bound_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
+      rho1 = round_bound(bound_bits, kBoundRes, s.n_rounds, s.n_ctiles, round);
+      rho2 = round_bound(bound_bits, kBoundLo, s.n_rounds, s.n_ctiles, round);
+    }
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
       uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32);
