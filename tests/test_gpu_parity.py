@@ -49,6 +49,8 @@ def test_hash_workloads(nat, name):
     (1, 2, 300, 64, 8192, 1, "bf16"),    # 128 column tiles
     (1, 1, 5, 64, 16384, 2, "bf16"),     # tiny L, maximum bucket count
     (3, 1, 129, 128, 256, 4, "f32"),
+    (1, 1, 300, 64, 16, 70, "bf16"),     # more rounds than the kernel keeps bound maxima for in LDS
+    (1, 2, 200, 128, 96, 65, "bf16"),
 ])
 def test_hash_shapes(nat, B, H, L, d, nb, r, dtype):
     _say(f"[hash-shape] B{B} H{H} L{L} d{d} b{nb} r{r} {dtype}")
