@@ -580,8 +580,9 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   };
   // Keys of tile n from acc: acc[i] is the projection on column
   // 32t + 8(i/4) + 4*half_sel + i%4.
-  auto keys_tile = [&](const f32x16 (&acc)[kStrips], int n) {
-    const int t = n % s.n_ctiles;
+  // Keys of the tile at column-tile index t of its round (tile n = round *
+  // n_ctiles + t).
+  auto keys_tile = [&](const f32x16 (&acc)[kStrips], int t) {
     const uint32_t tile_code = (static_cast<uint32_t>(t) << 5) | (static_cast<uint32_t>(half_sel) << 4);
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
@@ -601,9 +602,8 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   };
   // After the last tile of a round: merge the two lanes that share each
   // token, decide, flag near-ties.
-  auto round_end = [&](int n) {
-    const int round = n / s.n_ctiles;
-    if (n - round * s.n_ctiles != s.n_ctiles - 1) return;
+  auto round_end = [&](int t, int round) {
+    if (t != s.n_ctiles - 1) return;
     float cmax, rho1, rho2;
     if (rb_lds) {
       cmax = __uint_as_float(rbound[round][kBoundCmax]);
@@ -655,10 +655,11 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   // accumulators, no dependence), so one wavefront keeps the matrix core and
   // the vector ALU busy at once.
   f32x16 acc_a[kStrips], acc_b[kStrips];
+  int tp = 0, rp = 0;   // column tile and round of the tile whose keys the next step extracts
   auto step = [&](const u32x4* cur, u32x4* next, f32x16 (&acc)[kStrips], const f32x16 (&prev)[kStrips], int n) {
     dma_next(next, n);
     mfma_tile(acc, cur, n);
-    keys_tile(prev, n - 1);
+    keys_tile(prev, tp);
     // every LDS read of the tile's A operands first, so that none waits
     // behind the MFMAs; then one MFMA per five vector instructions
     __builtin_amdgcn_sched_group_barrier(0x100, kSteps + 2 * kLoSteps, 0);
@@ -667,7 +668,12 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then five vector instructions
     }
-    round_end(n - 1);
+    round_end(tp, rp);
+    // advance (tp, rp) to tile n, with scalar increments instead of a division per step
+    if (++tp == s.n_ctiles) {
+      tp = 0;
+      ++rp;
+    }
     __syncthreads();   // also makes every wavefront's near-tie pushes visible to the count below
   };
   dma_next(lds1, 0);
@@ -680,11 +686,11 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   }
   if (n < n_total) {   // n_total even: tile n (odd) is in lds1
     step(lds1, lds0, acc_b, acc_a, n);
-    keys_tile(acc_b, n);
+    keys_tile(acc_b, tp);
   } else {
-    keys_tile(acc_a, n - 1);
+    keys_tile(acc_a, tp);
   }
-  round_end(n_total - 1);
+  round_end(tp, rp);   // (tp, rp) is now the last tile's position
   __syncthreads();
   if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
 }
