@@ -60,6 +60,51 @@ def test_backward_matches_oracle(nat, L, d, r, nb, causal, dtype):
         assert ex <= tol and ev <= tol
 
 
+def _run_length(n_chunks, bh, n_cu=256):
+    """The host's choice of chunks per backward workgroup (restated here to
+    pick shapes that exercise each run length on a 256-CU part)."""
+    best, best_cost = 8, None
+    for run in (8, 16, 32):
+        wgs = -(-n_chunks // run) * bh
+        cost = -(-wgs // n_cu) * (run + 2)
+        if best_cost is None or cost < best_cost:
+            best, best_cost = run, cost
+    return best
+
+
+@pytest.mark.parametrize("B,H,L,d,r,run", [
+    (8, 8, 2560, 64, 2, 16),    # 40 chunks: runs of 16, 16 and 8
+    (14, 8, 3840, 64, 2, 32),   # 60 chunks: runs of 32 and 28
+])
+def test_backward_long_runs(nat, B, H, L, d, r, run):
+    """Grids large enough that the backward takes runs of 16 and 32 chunks per
+    workgroup (with a shorter last run); heads at both ends of the grid are
+    checked against the oracle."""
+    import torch
+
+    assert _run_length(L // 64, B * H) == run
+    _say(f"[bwd-run] B{B} H{H} L{L} d{d} r{r}: runs of {run}")
+    inp = W.custom_inputs(B, H, L, d, 16, r, dtype="bf16", seed=L + B)
+    qk, v, rot = to_device(inp)
+    b = nat.lsh_hash(qk, rot, 16)
+    perm, _ = nat.lsh_sort(b, 16)
+    out = nat.attend(qk, v, perm, 64, True)
+    g = np.random.default_rng(L + 7)
+    dbits = W.f32_to_bf16_bits(g.standard_normal((B, H, L, d)).astype(np.float32))
+    dout_h = W.bf16_bits_to_f32(dbits)
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    dqk, dv = nat.attend_backward(qk, v, perm, 64, True, out, dout)
+    dqk, dv = host(dqk), host(dv)
+    ph = host(perm)
+    for bi, h in ((0, 0), (B - 1, H - 1)):
+        _, wx, wv = oracle.lsh_attention_head_grad(inp.qk[bi, h].astype(np.float64), inp.v[bi, h].astype(np.float64),
+                                                   ph[bi, h], 64, True, dout_h[bi, h].astype(np.float64))
+        scale = max(1.0, float(np.abs(wx).max()), float(np.abs(wv).max()))
+        ex, ev = float(np.abs(dqk[bi, h] - wx).max()), float(np.abs(dv[bi, h] - wv).max())
+        _say(f"  ({bi}, {h}): max |dqk err| {ex:.2e}  max |dv err| {ev:.2e}  (scale {scale:.2f})")
+        assert ex <= 2e-2 * scale and ev <= 2e-2 * scale
+
+
 @pytest.mark.parametrize("L,d,r,causal,dtype", [
     (512, 64, 2, True, "f32"),
     (1024, 128, 3, True, "bf16"),
