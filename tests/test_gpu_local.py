@@ -49,6 +49,8 @@ def _device(arrs, bits):
     (1280, 64, 64, 1, 0, True, "f32"),       # two-slot ring, float32
     (1536, 128, 64, 1, 0, True, "f32"),      # two-slot ring, float32 at d = 128 (one workgroup per CU)
     (2000, 64, 40, 1, 0, True, "bf16"),      # ring with chunks across tile edges, ragged last tile
+    (1280, 64, 64, 0, 1, False, "bf16"),     # two-slot ring, windows reaching ahead (tile counts not regular)
+    (1520, 128, 40, 1, 0, True, "bf16"),     # two tiles in flight, three slots, d = 128, ragged last tile
 ])
 def test_local_attention_matches_oracle(nat, L, d, m, nb, na, causal, dtype):
     _say(f"[local] L{L} d{d} m{m} before{nb} after{na} causal={causal} {dtype}")
