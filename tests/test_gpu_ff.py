@@ -34,7 +34,8 @@ def _params(n, d, f, seed):
     return (x, w1, b1, w2, b2), (xd, w1d, torch.from_numpy(b1).cuda(), w2d, torch.from_numpy(b2).cuda())
 
 
-@pytest.mark.parametrize("n,d,f,chunk", [(300, 128, 256, 0), (1024, 256, 512, 128), (1000, 128, 384, 333)])
+@pytest.mark.parametrize("n,d,f,chunk", [(300, 128, 256, 0), (1024, 256, 512, 128), (1000, 128, 384, 333),
+                                         (600, 512, 1024, 0)])   # several 256-wide tiles, ragged rows
 def test_feed_forward_matches_oracle(nat, n, d, f, chunk):
     h, dev = _params(n, d, f, n + d + f)
     out = host(nat.feed_forward(*dev, chunk_tokens=chunk))
@@ -52,3 +53,4 @@ def test_chunking_changes_no_bit(nat):
     whole = nat.feed_forward(*dev, chunk_tokens=0)
     for chunk in (1, 7, 64, 129, 999, 1000, 5000):
         assert torch.equal(nat.feed_forward(*dev, chunk_tokens=chunk).view(torch.int16), whole.view(torch.int16)), chunk
+
