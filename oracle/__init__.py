@@ -21,6 +21,7 @@ from .local_oracle import (  # noqa: F401
 )
 from .backward_oracle import (  # noqa: F401
     dense_forward,
+    grad_positions,
     lsh_attention_head_grad,
     target_counts,
 )

@@ -70,3 +70,42 @@ def test_self_fallback_rows_pass_the_gradient_to_v():
     np.testing.assert_array_equal(dv[0], dout[0])
     np.testing.assert_array_equal(dv[1:], 0.0)
     np.testing.assert_array_equal(dx, 0.0)
+
+
+@pytest.mark.parametrize("L,d,r,nb,m,causal", [(32, 8, 2, 4, 8, False), (32, 8, 3, 4, 4, True),
+                                               (24, 4, 1, 2, 24, True), (16, 4, 2, 8, 1, False),
+                                               (64, 6, 4, 8, 8, True)])
+def test_sampled_gradients_equal_autograd(L, d, r, nb, m, causal):
+    """The per-position gradient (softmax derivative written out, observers
+    found from the chunk structure) equals autograd of the dense form at every
+    position, including self-fallback rows and keys seen in several rounds."""
+    x, v, perm = _case(L, d, r, nb, 5 * L + r)
+    dout = np.random.default_rng(L).standard_normal((L, d))
+    _, wx, wv = oracle.lsh_attention_head_grad(x, v, perm, m, causal, dout)
+    pos = np.random.default_rng(r).permutation(L)
+    gx, gv = oracle.grad_positions(x, v, perm, pos, m, causal, dout)
+    np.testing.assert_allclose(gx, wx[pos], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gv, wv[pos], rtol=0, atol=1e-12)
+
+
+def test_sampled_gradients_equal_finite_differences():
+    L, d, r, nb, m, causal = 16, 4, 2, 4, 4, True
+    x, v, perm = _case(L, d, r, nb, 99)
+    dout = np.random.default_rng(4).standard_normal((L, d))
+
+    def loss(xx, vv):
+        return float((oracle.lsh_attention_head(xx, vv, None, nb, m, causal, perm=perm)["out"] * dout).sum())
+
+    pos = [0, 5, L - 1]
+    gx, gv = oracle.grad_positions(x, v, perm, pos, m, causal, dout)
+    h = 1e-6
+    for n, i in enumerate(pos):
+        for k in range(d):
+            xp, xm = x.copy(), x.copy()
+            xp[i, k] += h
+            xm[i, k] -= h
+            assert abs((loss(xp, v) - loss(xm, v)) / (2 * h) - gx[n, k]) < 1e-6
+            vp, vm = v.copy(), v.copy()
+            vp[i, k] += h
+            vm[i, k] -= h
+            assert abs((loss(x, vp) - loss(x, vm)) / (2 * h) - gv[n, k]) < 1e-6

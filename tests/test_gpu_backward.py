@@ -105,6 +105,37 @@ def test_backward_long_runs(nat, B, H, L, d, r, run):
         assert ex <= 2e-2 * scale and ev <= 2e-2 * scale
 
 
+@pytest.mark.parametrize("name", ["text_64k", "image_12k"])
+def test_backward_full_size(nat, name):
+    """The backward at the full workload sizes, called as the benchmark times
+    it (the forward's log normaliser handed in): gradients at sampled
+    positions of the first and last heads against the per-position oracle."""
+    import torch
+
+    inp = W.make_inputs(name)
+    w = inp.workload
+    _say(f"[bwd-full] {name}: B{w.batch} H{w.heads} L{w.seq_len} d{w.d_head} r{w.n_rounds}")
+    qk, v, rot = to_device(inp)
+    perm, _ = nat.lsh_sort(nat.lsh_hash(qk, rot, w.n_buckets), w.n_buckets)
+    out, lse = nat.attend(qk, v, perm, w.chunk_len, w.causal, return_lse=True)
+    g = np.random.default_rng(w.index + 17)
+    dbits = W.f32_to_bf16_bits(g.standard_normal(tuple(v.shape), dtype=np.float32))
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    dqk, dv = nat.attend_backward(qk, v, perm, w.chunk_len, w.causal, out, dout, lse=lse)
+    torch.cuda.synchronize()
+    L = w.seq_len
+    rows = np.unique(np.concatenate([[0, 1, L - 1], g.integers(0, L, size=29)]))
+    for bi, h in ((0, 0), (w.batch - 1, w.heads - 1)):
+        wx, wv = oracle.grad_positions(inp.qk[bi, h].astype(np.float64), inp.v[bi, h].astype(np.float64),
+                                       host(perm[bi, h]), rows, w.chunk_len, w.causal,
+                                       W.bf16_bits_to_f32(dbits[bi, h]).astype(np.float64))
+        gx, gv = host(dqk[bi, h])[rows], host(dv[bi, h])[rows]
+        scale = max(1.0, float(np.abs(wx).max()), float(np.abs(wv).max()))
+        ex, ev = float(np.abs(gx - wx).max()), float(np.abs(gv - wv).max())
+        _say(f"  ({bi}, {h}): max |dqk err| {ex:.2e}  max |dv err| {ev:.2e}  (scale {scale:.2f})")
+        assert ex <= 2e-2 * scale and ev <= 2e-2 * scale
+
+
 @pytest.mark.parametrize("L,d,r,causal,dtype", [
     (512, 64, 2, True, "f32"),
     (1024, 128, 3, True, "bf16"),

@@ -84,3 +84,24 @@ def test_local_attention_overlaps_beyond_the_sequence(nat):
     big = host(nat.local_attention(qd, kd, vd, 32, 1 << 30, 1 << 30, False))
     want = oracle.local_attention(q, k, v, 32, 8, 8, False)
     np.testing.assert_allclose(big, want, rtol=0, atol=TOL["f32"])
+
+
+def test_local_attention_full_size(nat):
+    """The 64K text shape in the launch configuration the benchmark times
+    (batch 1, 8 heads, L = 65536, d = 128, chunks of 64 with one chunk of
+    look-back, causal, bf16): the first and last heads, every row."""
+    import torch
+
+    B, H, L, d = 1, 8, 65536, 128
+    _say(f"[local-full] B{B} H{H} L{L} d{d}")
+    g = np.random.default_rng(20200104)
+    bits = [W.f32_to_bf16_bits(g.standard_normal((B, H, L, d), dtype=np.float32)) for _ in range(3)]
+    q, k, v = _device(None, bits)
+    out = nat.local_attention(q, k, v, 64, 1, 0, True)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        qh, kh, vh = (W.bf16_bits_to_f32(b[0, h]).astype(np.float64) for b in bits)
+        want = oracle.local_attention_head(qh, kh, vh, 64, 1, 0, True)
+        err = float(np.abs(host(out[0, h]) - want).max())
+        _say(f"  head {h}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
