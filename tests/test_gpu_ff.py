@@ -54,3 +54,20 @@ def test_chunking_changes_no_bit(nat):
     for chunk in (1, 7, 64, 129, 999, 1000, 5000):
         assert torch.equal(nat.feed_forward(*dev, chunk_tokens=chunk).view(torch.int16), whole.view(torch.int16)), chunk
 
+
+
+def test_feed_forward_full_size(nat):
+    """The layer as `bench.py --ff` times it (65536 positions, d_model 1024,
+    d_ff 4096, chunks of 8192): the oracle works one position at a time, so
+    sampled rows (including the first and last of a chunk) are checked."""
+    n, d, f = 65536, 1024, 4096
+    h, dev = _params(n, d, f, 2020)
+    out = nat.feed_forward(*dev, chunk_tokens=8192)
+    rows = np.unique(np.concatenate([[0, 8191, 8192, n - 1], np.random.default_rng(1).integers(0, n, 60)]))
+    x, w1, b1, w2, b2 = h
+    want = oracle.feed_forward(x[rows], w1, b1, w2, b2)
+    got = host(out)[rows]
+    scale = max(1.0, float(np.abs(want).max()))
+    err = float(np.abs(got - want).max())
+    print(f"[ff-full] n{n} d{d} f{f}: max abs err on {rows.size} rows {err:.3e} (scale {scale:.2f})", flush=True)
+    assert err <= 1e-2 * scale
