@@ -377,6 +377,9 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
 __device__ __forceinline__ void lds_dma16(const u32x4* g, u32x4* l) {
 #if __HIP_DEVICE_COMPILE__
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+#else
+  (void)g;
+  (void)l;
 #endif
 }
 
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; smax[st] = INT32_MIN; }
 
   // Projections of tile n (lds buffer n & 1) into acc.
-  auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur, int n) {
+  auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur) {
 #pragma unroll
     for (int st = 0; st < kStrips; ++st)
 #pragma unroll
@@ -658,7 +661,7 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
   int tp = 0, rp = 0;   // column tile and round of the tile whose keys the next step extracts
   auto step = [&](const u32x4* cur, u32x4* next, f32x16 (&acc)[kStrips], const f32x16 (&prev)[kStrips], int n) {
     dma_next(next, n);
-    mfma_tile(acc, cur, n);
+    mfma_tile(acc, cur);
     keys_tile(prev, tp);
     // every LDS read of the tile's A operands first, so that none waits
     // behind the MFMAs; then one MFMA per five vector instructions
@@ -677,7 +680,7 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
     __syncthreads();   // also makes every wavefront's near-tie pushes visible to the count below
   };
   dma_next(lds1, 0);
-  mfma_tile(acc_a, lds0, 0);
+  mfma_tile(acc_a, lds0);
   __syncthreads();
   int n = 1;
   for (; n + 1 < n_total; n += 2) {
