@@ -34,12 +34,64 @@ struct alignas(16) FfLds {
   uint16_t x[2][kFT * kFPitch];
 };
 
+// Workgroup -> output tile.  Workgroups are dispatched to the 8 XCDs in turn
+// (workgroup b to XCD b % 8), and each XCD has its own L2.  The tile grid is
+// cut into pm x pn blocks, one per XCD; an XCD walks its block in groups of
+// kFGroup tile rows, sweeping the columns with the rows of a group innermost,
+// so the 64 workgroups an XCD holds at once cover about 8 x 8 tiles and a
+// group's rows of X stay in L2 for the whole sweep.  pm == 0: row-major order.
+constexpr int kFGroup = 8;
+
+struct FfTileOrder {
+  int mt, nt;   // tiles along M and N
+  int pm, pn;   // XCD blocks along M and N (pm * pn == 8), or pm == 0
+
+  __device__ __forceinline__ void tile_of(int b, int& m, int& n) const {
+    if (pm == 0) {
+      m = b / nt;
+      n = b - m * nt;
+      return;
+    }
+    const int xcd = b & 7, local = b >> 3;
+    const int bm = mt / pm, bn = nt / pn;
+    const int group = local / (kFGroup * bn), idx = local - group * kFGroup * bn;
+    const int gsize = min(kFGroup, bm - group * kFGroup);
+    const int ln = idx / gsize, lm = group * kFGroup + (idx - ln * gsize);
+    m = (xcd / pn) * bm + lm;
+    n = (xcd % pn) * bn + ln;
+  }
+};
+
+// The even split with the least L2 fill traffic per XCD, counted in tile rows
+// of 128 x K: its rows of X once, and its columns of W once if they fit in
+// about half of the 4 MB L2, else once per group of rows.
+FfTileOrder ff_tile_order(int mt, int nt, int K) {
+  FfTileOrder o{mt, nt, 0, 1};
+  long best = 0;
+  const long tile_bytes = static_cast<long>(kFT) * K * 2;
+  for (int pm = 1; pm <= 8; pm *= 2) {
+    const int pn = 8 / pm;
+    if (mt % pm != 0 || nt % pn != 0) continue;
+    const int bm = mt / pm, bn = nt / pn;
+    const bool w_fits = bn * tile_bytes <= (2l << 20);
+    const long cost = bm + static_cast<long>(bn) * (w_fits ? 1 : (bm + kFGroup - 1) / kFGroup);
+    if (best == 0 || cost < best) {
+      best = cost;
+      o.pm = pm;
+      o.pn = pn;
+    }
+  }
+  return o;
+}
+
 template <bool RELU>
 __global__ __launch_bounds__(256, 2) void linear_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                         const float* __restrict__ bias, int M, int N, int K,
-                                                        uint16_t* __restrict__ Y) {
+                                                        uint16_t* __restrict__ Y, FfTileOrder order) {
   __shared__ FfLds sh;
-  const int n_blk = blockIdx.x * kFT, m_blk = blockIdx.y * kFT;
+  int m_tile, n_tile;
+  order.tile_of(blockIdx.x, m_tile, n_tile);
+  const int n_blk = n_tile * kFT, m_blk = m_tile * kFT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int wn = 64 * (wave & 1), wm = 64 * (wave >> 1);
@@ -124,8 +176,9 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(const uint16_t* __restri
 template <bool RELU>
 void launch_linear(const uint16_t* X, const uint16_t* W, const float* bias, int M, int N, int K, uint16_t* Y,
                    hipStream_t stream) {
-  dim3 grid(N / kFT, (M + kFT - 1) / kFT);
-  hipLaunchKernelGGL((linear_kernel<RELU>), grid, dim3(256), 0, stream, X, W, bias, M, N, K, Y);
+  const int mt = (M + kFT - 1) / kFT, nt = N / kFT;
+  hipLaunchKernelGGL((linear_kernel<RELU>), dim3(mt * nt), dim3(256), 0, stream, X, W, bias, M, N, K, Y,
+                     ff_tile_order(mt, nt, K));
 }
 
 }  // namespace
