@@ -64,7 +64,7 @@ struct FfTileOrder {
 
 // The even split with the least L2 fill traffic per XCD, counted in tile rows
 // of 128 x K: its rows of X once, and its columns of W once if they fit in
-// about half of the 4 MB L2, else once per group of rows.
+// the 4 MB L2, else once per group of rows.
 FfTileOrder ff_tile_order(int mt, int nt, int K) {
   FfTileOrder o{mt, nt, 0, 1};
   long best = 0;
@@ -73,7 +73,7 @@ FfTileOrder ff_tile_order(int mt, int nt, int K) {
     const int pn = 8 / pm;
     if (mt % pm != 0 || nt % pn != 0) continue;
     const int bm = mt / pm, bn = nt / pn;
-    const bool w_fits = bn * tile_bytes <= (2l << 20);
+    const bool w_fits = bn * tile_bytes <= (4l << 20);
     const long cost = bm + static_cast<long>(bn) * (w_fits ? 1 : (bm + kFGroup - 1) / kFGroup);
     if (best == 0 || cost < best) {
       best = cost;
