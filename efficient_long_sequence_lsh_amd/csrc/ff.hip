@@ -27,7 +27,11 @@ namespace {
 
 constexpr int kFT = 128;       // rows and columns of a workgroup tile
 constexpr int kFK = 64;        // K per LDS block
-constexpr int kFPitch = kFK + 8;   // bf16 per LDS row (16-byte pad)
+constexpr int kFPitch = kFK;       // bf16 per LDS row: 8 pieces of 16 bytes, no pad
+// Piece p of row r sits in slot p ^ ((r >> 1) & 7): the 16 lanes of an MFMA
+// operand read (rows r0 .. r0 + 15, one piece) and of a tile copy store (two
+// rows, all eight pieces) each touch 16 different 4-bank groups.
+__device__ __forceinline__ int ff_slot(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
 struct alignas(16) FfLds {
   uint16_t w[2][kFT * kFPitch];
@@ -111,8 +115,8 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(const uint16_t* __restri
     for (int i = 0; i < 4; ++i) {
       const int u = threadIdx.x + 256 * i;
       const int row = u >> 3, pc = u & 7;
-      *reinterpret_cast<u32x4*>(&sh.w[buf][row * kFPitch + 8 * pc]) = wr[i];
-      *reinterpret_cast<u32x4*>(&sh.x[buf][row * kFPitch + 8 * pc]) = xr[i];
+      *reinterpret_cast<u32x4*>(&sh.w[buf][row * kFPitch + 8 * ff_slot(row, pc)]) = wr[i];
+      *reinterpret_cast<u32x4*>(&sh.x[buf][row * kFPitch + 8 * ff_slot(row, pc)]) = xr[i];
     }
   };
 
@@ -137,9 +141,9 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(const uint16_t* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               &sh.w[buf][(wn + 16 * i + c16) * kFPitch + 32 * ks + 8 * g]));
+                                               &sh.w[buf][(wn + 16 * i + c16) * kFPitch + 8 * ff_slot(c16, 4 * ks + g)]));
         bfr[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                &sh.x[buf][(wm + 16 * i + c16) * kFPitch + 32 * ks + 8 * g]));
+                                                &sh.x[buf][(wm + 16 * i + c16) * kFPitch + 8 * ff_slot(c16, 4 * ks + g)]));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
