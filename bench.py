@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--local-chunk", type=int, default=64)
     ap.add_argument("--local-before", type=int, default=1)
     ap.add_argument("--local-after", type=int, default=0)
+    ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output of --profile-stage full and of "
+                         "--profile-stage copy for --workload, and record calibrated HBM bytes per launch of each "
+                         "kernel (with its source digest) in profiles/traffic.json")
     ap.add_argument("--profile-stage", choices=["full", "hash", "sort", "attend", "combine", "copy"],
                     help="profiling mode: run the prerequisite stages once, then only this stage --steps times "
                          "(copy = a plain 256 MiB device copy for counter calibration); prints its timing")
@@ -124,11 +128,12 @@ class Stages:
                                                        arr, len(events), self.stream()),
                  "reformer_lsh_attention_timed")
 
-    def hash(self):
+    def hash(self, ties=None):
         B, H, L, d, r, nb = self.shape
         self._ok(self.lib.reformer_lsh_hash(self.qk.data_ptr(), self.dtype, self.rot.data_ptr(), B, H, L, d, r, nb,
-                                            self.buckets.data_ptr(), None, self.hash_ws.data_ptr(), self.hash_ws_n,
-                                            self.stream()), "reformer_lsh_hash")
+                                            self.buckets.data_ptr(), None if ties is None else ties.data_ptr(),
+                                            self.hash_ws.data_ptr(), self.hash_ws_n, self.stream()),
+                 "reformer_lsh_hash")
 
     def sort(self):
         B, H, L, d, r, nb = self.shape
@@ -254,17 +259,92 @@ def measured_traffic(kernel, src, w):
     return ent.get("bytes_per_launch")
 
 
+KERNEL_SOURCES = {"hash_": "hash.hip", "sort_": "sort.hip", "chunk_attend": "attend.hip", "combine_": "combine.hip"}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_KIB = 262144   # --profile-stage copy moves 256 MiB each way
+
+
+def _kernel_key(name: str) -> str:
+    """Kernel key as the bench names it, from a demangled rocprofv3 kernel name."""
+    base = name.replace("(anonymous namespace)", "").split("(")[0]
+    ident = base.split("<")[0].split("::")[-1].strip()
+    if ident == "chunk_attend64_kernel" and "<" in base:
+        mode = int(base.split("<", 1)[1].rstrip(">").split(",")[-1])
+        return ident + ("" if mode == 0 else "<compact>" if mode == 1 else "<final>")
+    return ident
+
+
+def _counter_means(folder: str, counter: str) -> dict:
+    """Mean counter value per dispatch of each kernel in a rocprofv3 csv run."""
+    import csv
+    import glob
+
+    sums, counts = {}, {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {folder}")
+    for path in files:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                k = row["Kernel_Name"]
+                sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def ingest_traffic(args):
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.ingest_traffic
+    cf = _counter_means(cfetch_dir, "FETCH_SIZE")
+    cw = _counter_means(cwrite_dir, "WRITE_SIZE")
+    copy_f = [v for k, v in cf.items() if COPY_KERNEL in k]
+    copy_w = [v for k, v in cw.items() if COPY_KERNEL in k]
+    if not copy_f or not copy_w:
+        raise SystemExit(f"no {COPY_KERNEL} dispatches in the calibration runs")
+    ff, wf = COPY_KIB / copy_f[0], COPY_KIB / copy_w[0]
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    entries = {}
+    for name, fk in fetch.items():
+        key = _kernel_key(name)
+        src = next((v for p, v in KERNEL_SOURCES.items() if key.startswith(p)), None)
+        wk = next((v for n, v in write.items() if _kernel_key(n) == key), None)
+        if src is None or wk is None:
+            continue
+        entries[key] = {"bytes_per_launch": int(round((fk * ff + wk * wf) * 1024)), "fetch_factor": round(ff, 4),
+                        "fetch_kib": round(fk, 1), "source": src,
+                        "source_sha256_16": source_digest(os.path.join(ROOT, "efficient_long_sequence_lsh_amd",
+                                                                       "csrc", src)),
+                        "write_factor": round(wf, 4), "write_kib": round(wk, 1)}
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data.setdefault(args.workload, {}).update(entries)
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({"workload": args.workload, "fetch_factor": ff, "write_factor": wf, "kernels": entries}, indent=1))
+
+
 def cpu_baseline(w, inp, heads):
-    """The float64 oracle on `heads` (batch, head) slices of the same workload."""
+    """The float64 oracle on `heads` (batch, head) slices of the same workload.
+
+    Returns the baseline record and the oracle's results per slice (bucket
+    ids, margins, permutation and output), which the parity check compares
+    with the GPU's."""
     import numpy as np
 
     import oracle
 
     pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)][:heads]
+    results = {}
     t0 = time.perf_counter()
     for b, h in pairs:
-        oracle.lsh_attention_head(inp.qk[b, h].astype(np.float64), inp.v[b, h].astype(np.float64), inp.rotations,
-                                  w.n_buckets, w.chunk_len, w.causal)
+        results[(b, h)] = oracle.lsh_attention_head(inp.qk[b, h].astype(np.float64), inp.v[b, h].astype(np.float64),
+                                                    inp.rotations, w.n_buckets, w.chunk_len, w.causal)
     dt = time.perf_counter() - t0
     frac = len(pairs) / (w.batch * w.heads)       # share of one forward pass the sample covers
     value = w.tokens * frac / dt
@@ -278,7 +358,73 @@ def cpu_baseline(w, inp, heads):
     return {"value": round(value, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(pairs)} of {w.batch * w.heads} (batch, head) slices, full length {w.seq_len}, "
                       f"all {w.n_rounds} rounds; {dt:.1f} s wall; value = covered share of one forward's "
-                      f"{w.tokens} tokens / wall time"}
+                      f"{w.tokens} tokens / wall time"}, results
+
+
+NEAR_TIE = 1e-5
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def parity_vs_oracle(st, w, results):
+    """The GPU's bucket ids, permutation and output against the oracle's on the
+    slices the CPU baseline ran (every position, every round of each slice).
+
+    bucket_flips counts differing ids; near_ties_lt_1e-5 the (position, round)
+    pairs whose exact top-two gap is below 1e-5 (where a flip is allowed);
+    flips_at_margin_ge_1e-5 must be 0.  redecided is the GPU's own count of
+    float64 re-decisions over the whole workload.  perm_exact compares the
+    GPU's sort with the oracle's; max_abs_err the pipeline's output with the
+    oracle's (both only meaningful without flips, else they are taken against
+    the oracle's sort of the GPU ids and reported as null respectively)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    ties = torch.zeros(1, dtype=torch.int32, device=st.qk.device)
+    st.hash(ties)
+    st.sort()
+    st.full()
+    torch.cuda.synchronize()
+    gb = st.buckets.cpu().numpy()
+    gp = st.perm.cpu().numpy()
+    out = st.out.float().cpu().numpy()
+    n_ids = flips = near = bad = 0
+    perm_ok = True
+    err = 0.0
+    for (b, h), res in results.items():
+        ob, om = res["buckets"], res["margin"]
+        mism = gb[b, h] != ob
+        n_ids += mism.size
+        flips += int(mism.sum())
+        near += int((om < NEAR_TIE).sum())
+        bad += int((mism & (om >= NEAR_TIE)).sum())
+        want_p = res["perm"] if not mism.any() else oracle.lsh_sort(gb[b, h])[0]
+        perm_ok &= bool(np.array_equal(gp[b, h], want_p))
+        if not mism.any():
+            err = max(err, float(np.abs(out[b, h] - res["out"]).max()))
+    return {"slices": len(results), "bucket_ids": n_ids, "bucket_flips": flips, "near_ties_lt_1e-5": near,
+            "flips_at_margin_ge_1e-5": bad, "redecided": int(ties.item()), "perm_exact": perm_ok,
+            "max_abs_err": round(err, 6) if flips == 0 else None, "tol": TOL[w.dtype],
+            "pass": bad == 0 and perm_ok and (flips > 0 or err <= TOL[w.dtype])}
+
+
+def peak_memory(nat, w, qk, v, rot):
+    """Device memory of one forward pass: inputs resident, then the output and
+    the workspace allocated and the pipeline run (torch's allocator counts
+    every device allocation the pass makes)."""
+    import torch
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws_n = nat.workspace_bytes(w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds, w.n_buckets, w.chunk_len,
+                               nat._dtype_code(qk))
+    nat.attention(qk, v, rot, w.n_buckets, w.chunk_len, w.causal)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    return {"peak_allocated_bytes": int(peak), "inputs_bytes": int(base), "workspace_bytes": int(ws_n),
+            "out_bytes": int(v.numel() * v.element_size()), "peak_gib": round(peak / 2 ** 30, 3)}
 
 
 def profile_stage(args, st, w):
@@ -524,6 +670,9 @@ def main():
               "the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
+    if args.ingest_traffic:
+        ingest_traffic(args)
+        return
     if args.accuracy_sweep:
         accuracy_sweep(args)
         return
@@ -557,6 +706,7 @@ def main():
         qk = torch.from_numpy(inp.qk).cuda()
         v = torch.from_numpy(inp.v).cuda()
     rot = torch.from_numpy(inp.rotations).cuda()
+    memory = None if args.profile_stage else peak_memory(nat, w, qk, v, rot)
     st = Stages(nat, w, qk, v, rot)
     if args.profile_stage:
         profile_stage(args, st, w)
@@ -566,17 +716,26 @@ def main():
     for _ in range(args.warmup):
         st.full()
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps on the launch stream: the total
+    # over the K steps gives ms_per_step, the per-step spans the spread
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    s.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         st.full()
-    e.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     value = w.tokens / (ms / 1e3)
-    log(args, f"[bench] {ms:.3f} ms/step, {value:.4g} tokens/s")
+
+    def pct(q):
+        return round(per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))], 4)
+
+    spread = {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9), "min": round(per_step[0], 4),
+              "max": round(per_step[-1], 4)}
+    log(args, f"[bench] {ms:.3f} ms/step (median {spread['median']}, p10 {spread['p10']}, p90 {spread['p90']}), "
+              f"{value:.4g} tokens/s")
 
     # Per-kernel durations of the pipeline's own launches: HIP events recorded
     # by the library at its kernel boundaries on this stream, every timed step.
@@ -606,10 +765,12 @@ def main():
     stages["hash_setup"] = {"ms": round(stage_ms["hash_setup"], 4)}
     stages["hash_fixup"] = {"ms": round(stage_ms["hash_fixup"], 4)}
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         log(args, f"[bench] cpu baseline: oracle on {args.cpu_heads} slices")
-        cpu = cpu_baseline(w, inp, args.cpu_heads)
+        cpu, results = cpu_baseline(w, inp, args.cpu_heads)
+        parity = parity_vs_oracle(st, w, results)
+        log(args, f"[bench] parity: {parity}")
 
     line = {
         "metric": "LSH-attention fwd tokens/sec at L=64K, 4 rounds; % of HBM/MFMA roofline",
@@ -628,8 +789,11 @@ def main():
                    "n_buckets": w.n_buckets, "chunk_len": w.chunk_len, "n_rounds": w.n_rounds, "causal": w.causal,
                    "qk": w.qk_kind},
         "roofline": roof,
+        "ms_per_step_spread": spread,
+        "memory": memory,
         "stages": stages,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
 

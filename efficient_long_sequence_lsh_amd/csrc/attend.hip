@@ -1,10 +1,10 @@
 // Stages 3 + 4: gather sorted rows and run chunked attention for every round.
 //
 // "Reformer: The Efficient Transformer" (research summary), Key points:
-//   LSH attention bullet -- after sorting, each chunk of m positions attends to
-//   itself and to the chunk before it;
-//   Shared-QK bullet -- queries and keys are the same vectors, and a token does
-//   not attend to itself unless it has no other valid target (the fallback is
+//   LSH attention bullet -- the sorted positions form chunks of m whose queries
+//   see the keys of their own chunk and of the preceding one;
+//   Shared-QK bullet -- queries and keys are the same vectors, and a position's
+//   own key is excluded unless nothing else is left for it (that fallback is
 //   applied when the rounds are combined).
 // Readings where the page is silent: score x_i.x_j / sqrt(d); chunk 0 has no
 // predecessor; optional causal mask by original position (key j < query i);

@@ -2,9 +2,9 @@
 // qk and the values v, for a given sorted order (the hash is held fixed: bucket
 // ids are piecewise constant in the inputs).
 //
-// "Reformer: The Efficient Transformer" (research summary), Key points: after
-// sorting, each chunk of m positions attends to itself and the chunk before it
-// (LSH attention bullet); a token attends to itself only when it has no other
+// "Reformer: The Efficient Transformer" (research summary), Key points: the
+// sorted positions form chunks of m whose queries see their own chunk's and the
+// preceding chunk's keys (LSH attention bullet); a token attends to itself only when it has no other
 // target (Shared-QK bullet); several rounds are combined (Number of hash
 // rounds bullet; combined here with logsumexp weights).  With Z_i the
 // logsumexp of the scores of all (round, key) pairs query i sees, the forward

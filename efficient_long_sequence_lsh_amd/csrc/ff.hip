@@ -1,9 +1,9 @@
 // Position-wise feed-forward layer applied in chunks of positions.
 //
 // "Reformer: The Efficient Transformer" (research summary), Summary and Key
-// points (reversible layers bullet): the feed-forward layers are processed in
-// chunks, which removes the d_ff factor from activation memory and gives
-// numerically identical results.  Here y = relu(x W1^T + b1) W2^T + b2 (the
+// points (reversible layers bullet): the feed-forward layers run over a chunk
+// of positions at a time, so the d_ff-wide activation is never held for the
+// whole sequence, and the results stay the same.  Here y = relu(x W1^T + b1) W2^T + b2 (the
 // pages name no activation; ReLU is the plainest reading), with the d_ff-wide
 // intermediate of one chunk at a time held in the caller's workspace.
 //

@@ -20,16 +20,20 @@
 //     turned into an ordered 32-bit key with one and-or: the float's bits with
 //     the sign cleared and a candidate code in the low mantissa bits.  A
 //     running top-two of keys per lane takes a med3, a max and a max3 per two
-//     values.  The sign is left out of the keys: a running maximum of the raw
+//     values; once per tile the lane's top two are merged into a running top
+//     three.  The sign is left out of the keys: a running maximum of the raw
 //     float bits as signed integers (a max3 per two values) tells at the end
 //     of the round whether the winner is positive -- it is exactly when that
 //     maximum reaches the winner's magnitude.  The two lanes sharing a token
 //     merge once per round.
-//   * The top-two keys give the two leading candidates and their gap.  When the
-//     gap is below twice a bound on the error of one projection, the
-//     (position, round) is queued and a fix-up kernel re-decides it in float64
-//     between those two candidates (or over all columns when even the leading
-//     magnitude is within the bound, e.g. x = 0).  By Cauchy-Schwarz, with x6
+//   * The leading keys give the two leading candidates and their gap.  When the
+//     gap is below twice a bound on the error of one projection (plus the key
+//     truncation), the (position, round) is queued and a fix-up kernel
+//     re-decides it in float64: between those two candidates when the third
+//     key is provably more than the bound below the leader, otherwise over all
+//     columns (keys rank candidates that share a truncation bin by code, not
+//     by value, so only a bound on everything outside the top two makes the
+//     pair re-decision exact).  By Cauchy-Schwarz, with x6
 //     and R_lo6 the fp6 operands, one projection is off by at most
 //       |x| max_j |R_j - R_hi,j - R_lo6,j| + |x - x6| max_j |R_lo6,j|
 //     plus float32 accumulation (below 2^-15 (|x| max_j |R_j| + |x6| max_j
@@ -81,15 +85,31 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
 }
 
-__device__ __forceinline__ void top2_push(uint32_t& k1, uint32_t& k2, uint32_t key) {
+// Exact top-three of single keys (float32 path): k1 >= k2 >= k3.
+__device__ __forceinline__ void top3_push(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t key) {
+  k3 = umed3(k2, k3, key);
   k2 = umed3(k1, k2, key);
   k1 = max(k1, key);
 }
 
-__device__ __forceinline__ void top2_merge(uint32_t& k1, uint32_t& k2, uint32_t o1, uint32_t o2) {
-  uint32_t n2 = max(min(k1, o1), max(k2, o2));
-  k1 = max(k1, o1);
+// The three largest of {k1 >= k2 >= k3} and a sorted pair {a >= b}: the n-th
+// largest of two sorted lists is the largest min(A_i, B_j) over i + j = n.
+__device__ __forceinline__ void top3_merge2(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t a, uint32_t b) {
+  const uint32_t n3 = max(max(k3, min(k2, a)), min(k1, b));
+  const uint32_t n2 = max(min(k1, a), max(k2, b));
+  k1 = max(k1, a);
   k2 = n2;
+  k3 = n3;
+}
+
+// The three largest of two sorted triples.
+__device__ __forceinline__ void top3_merge3(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t a1, uint32_t a2,
+                                            uint32_t a3) {
+  const uint32_t n3 = max(max(max(k3, a3), min(k2, a1)), min(k1, a2));
+  const uint32_t n2 = max(min(k1, a1), max(k2, a2));
+  k1 = max(k1, a1);
+  k2 = n2;
+  k3 = n3;
 }
 
 __device__ __forceinline__ float key_magnitude(uint32_t key, uint32_t code_mask) {
@@ -102,40 +122,69 @@ constexpr int kTokensPerBlock = 256;
 
 struct NearTieList {
   int32_t* counts;    // per workgroup: number of queued entries
-  int32_t* entries;   // 3 per entry: token, round | full<<31, c1 | c2<<16
+  int32_t* entries;   // 3 per entry: token, round | kind<<30, c1 | c2<<16
   int cap;            // entries per workgroup region
   int* lds_count;     // the workgroup's counter in LDS (set inside the kernel)
 };
 
-__device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int round, bool full, int c1, int c2) {
+// What a queued (position, round) is re-decided over.
+enum NearTieKind : int {
+  kTiePair = 0,    // the two leading candidates c1, c2
+  kTieGroup = 1,   // the 16 columns of c1's group (one lane's projections of one tile)
+  kTieFull = 2,    // every column
+};
+
+__device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int round, int kind, int c1, int c2) {
   int idx = atomicAdd(lst.lds_count, 1);
   int32_t* e = lst.entries + 3 * (static_cast<size_t>(blockIdx.x) * lst.cap + idx);
   e[0] = tok;
-  e[1] = round | (full ? static_cast<int>(0x80000000u) : 0);
+  e[1] = round | (kind << 30);
   e[2] = (c1 & 0xffff) | (c2 << 16);
 }
 
-// Shared decision once a token's top-two keys and |x|_2 are known.
+// Shared decision once a token's three leading keys and |x|_2 are known.
 // tau_x bounds the error of the gap between two projections before key
-// truncation, which is added here.  smax is the largest raw projection bit
-// pattern as a signed integer (the largest positive projection, if any): the
-// winner is positive exactly when smax reaches its truncated magnitude.  Were
-// the winner negative while a positive projection reached that magnitude, the
-// two would share a truncated magnitude, so the gap would be zero and the
-// fix-up would decide.
-__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, int32_t smax, int col1, int col2,
-                                                 float tau_x, int code_bits, int half, int tok, int seq_len,
-                                                 int n_rounds, int round, int32_t* buckets, NearTieList lst) {
+// truncation, which is added here.  Keys order candidates by truncated
+// magnitude and, inside one truncation bin, by candidate code, so a candidate
+// can rank below others whose projections are smaller.
+//
+// k3 is the third of the union of every group's top two keys (a group is one
+// lane's 16 projections of one tile in the MFMA kernel, a single projection
+// in the float32 kernel).  When k1 and k2 come from different groups, k3 is
+// the overall third key, so every candidate outside the top two has a
+// truncated magnitude at most m3.  When they come from one group G, every
+// candidate outside G is at most m3 (its group's best key is in the union
+// below k1, k2), but G's own third is unknown.  So:
+//   m1 - m2 > tau                  -> the leader wins outright;
+//   else m1 - m3 > tau, two groups -> float64 re-decision between the top two;
+//   else m1 - m3 > tau, one group  -> float64 re-decision over G's columns;
+//   else                           -> float64 re-decision over all columns
+// (also when even the leader's magnitude is within tau, e.g. x = 0).  smax is
+// the largest raw projection bit pattern as a signed integer (the largest
+// positive projection, if any): the winner is positive exactly when smax
+// reaches its truncated magnitude.  Were the winner negative while a positive
+// projection reached that magnitude, the two would share a truncated
+// magnitude, so the gap would be zero and the fix-up would decide.
+__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, uint32_t k3, bool same_group, int32_t smax,
+                                                 int col1, int col2, float tau_x, int code_bits, int half, int tok,
+                                                 int seq_len, int n_rounds, int round, int32_t* buckets,
+                                                 NearTieList lst) {
   const uint32_t code_mask = (1u << code_bits) - 1u;
-  float m1 = key_magnitude(k1, code_mask);
-  float m2 = key_magnitude(k2, code_mask);
-  float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
+  const float m1 = key_magnitude(k1, code_mask);
+  const float m2 = key_magnitude(k2, code_mask);
+  const float m3 = key_magnitude(k3, code_mask);
+  const float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
   const bool positive = smax >= static_cast<int32_t>(k1 & ~code_mask);
-  int bucket = col1 + (positive ? 0 : half);
-  int bh = tok / seq_len, pos = tok - bh * seq_len;
+  const int bucket = col1 + (positive ? 0 : half);
+  const int bh = tok / seq_len, pos = tok - bh * seq_len;
   buckets[(static_cast<size_t>(bh) * n_rounds + round) * seq_len + pos] = bucket;
-  bool full = !(m1 > tau);
-  if (full || (m1 - m2) <= tau) push_near_tie(lst, tok, round, full, col1, col2);
+  const bool tiny = !(m1 > tau);
+  const bool near = !((m1 - m2) > tau);
+  const bool third_far = (m1 - m3) > tau;
+  if (tiny || near) {
+    const int kind = (tiny || !third_far) ? kTieFull : same_group ? kTieGroup : kTiePair;
+    push_near_tie(lst, tok, round, kind, col1, col2);
+  }
 }
 
 // The float32 bounds assume that the products and partial sums that matter
@@ -549,10 +598,13 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
 
   const uint32_t code_mask = (1u << s.code_bits) - 1u;
   const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
-  uint32_t k1[kStrips], k2[kStrips];
+  // Running top three of the per-lane, per-tile top twos (a "group" is one
+  // lane's 16 projections of one tile): the overall third-largest key is k3
+  // unless k1 and k2 come from the same group (see round_end).
+  uint32_t k1[kStrips], k2[kStrips], k3[kStrips];
   int32_t smax[kStrips];
 #pragma unroll
-  for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; smax[st] = INT32_MIN; }
+  for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; k3[st] = 0u; smax[st] = INT32_MIN; }
 
   // Projections of tile n (lds buffer n & 1) into acc.
   auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur) {
@@ -600,7 +652,7 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
         sm = max(max(sm, __float_as_int(acc[st][i])), __float_as_int(acc[st][i + 1]));
       }
       smax[st] = sm;
-      top2_merge(k1[st], k2[st], t1 | tile_code, t2 | tile_code);
+      top3_merge2(k1[st], k2[st], k3[st], t1 | tile_code, t2 | tile_code);
     }
   };
   // After the last tile of a round: merge the two lanes that share each
@@ -619,8 +671,8 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
     }
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
-      uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32);
-      top2_merge(k1[st], k2[st], o1, o2);
+      const uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32), o3 = shfl_xor_u(k3[st], 32);
+      top3_merge3(k1[st], k2[st], k3[st], o1, o2, o3);
       const int32_t sm = max(smax[st], static_cast<int32_t>(shfl_xor_u(static_cast<uint32_t>(smax[st]), 32)));
       int tok = tok_base + 32 * st + lane;
       if (lane < 32 && tok < s.n_tokens) {
@@ -631,12 +683,16 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
           uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
           return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
         };
-        decide_and_store(k1[st], k2[st], sm, col_of(c1), col_of(c2),
+        // a group is one lane's 16 projections of one tile: code >> 4 is
+        // (tile, lane half)
+        const bool same_group = ((c1 ^ c2) >> 4) == 0u;
+        decide_and_store(k1[st], k2[st], k3[st], same_group, sm, col_of(c1), col_of(c2),
                          split_gap_bound(xn.x, xn.y, cmax, rho1, rho2), s.code_bits, s.half, tok, s.seq_len,
                          s.n_rounds, round, buckets, lst);
       }
       k1[st] = 0u;
       k2[st] = 0u;
+      k3[st] = 0u;
       smax[st] = INT32_MIN;
     }
   };
@@ -723,7 +779,7 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
   const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
   for (int round = 0; round < s.n_rounds; ++round) {
     const float* R = rot + static_cast<size_t>(round) * D * s.half;
-    uint32_t k1 = 0u, k2 = 0u;
+    uint32_t k1 = 0u, k2 = 0u, k3 = 0u;
     int32_t smax = INT32_MIN;
     for (int c0 = 0; c0 < s.half; c0 += kCols) {
       __syncthreads();
@@ -736,14 +792,14 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
         float p = 0.0f;
 #pragma unroll
         for (int k = 0; k < D; ++k) p = fmaf(x[k], rt[k][j], p);
-        top2_push(k1, k2, make_key(p, keep_mask, static_cast<uint32_t>(c0 + j)));
+        top3_push(k1, k2, k3, make_key(p, keep_mask, static_cast<uint32_t>(c0 + j)));
         smax = max(smax, __float_as_int(p));
       }
     }
     const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
     if (live) {
       int c1 = static_cast<int>(k1 & code_mask), c2 = static_cast<int>(k2 & code_mask);
-      decide_and_store(k1, k2, smax, c1, c2, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
+      decide_and_store(k1, k2, k3, false, smax, c1, c2, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
                        s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
@@ -752,20 +808,52 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------- fix-up ----
-// Re-decide queued (token, round) pairs in float64 (products of a bf16 or
-// float32 feature and a float32 rotation entry are exact in float64).  A group
-// of 16 lanes takes one entry: for a pair, lane i holds features
-// [i*D/16, (i+1)*D/16) and the two column dot products are summed across the
-// group; for a full rescore, lane i scores columns i, i+16, ...
+// Re-decide queued (token, round) pairs in float64: products of a bf16 or
+// float32 feature and a float32 rotation entry are exact in float64, and a
+// D-term sum rounds by at most about D * 2^-53 of |x| max_j |R_j|.
+//  * pair and group entries take one group of 16 lanes each.  Pair: lane i
+//    holds features [i*D/16, (i+1)*D/16) and the two column dot products are
+//    summed across the 16 lanes.  Group: lane i scores column i of the group
+//    (a whole dot product, the column read from the transposed copy).
+//  * full entries take the whole workgroup: x staged in LDS as float64,
+//    thread t scores columns t, t + 256, ... with the rotations in their
+//    original [k][column] layout (a wavefront reads 64 consecutive floats per
+//    feature), then a workgroup reduction.
+// Best candidate as (value, bucket): the larger value wins, equal values go
+// to the lower bucket; p == 0 counts as +p (the lower bucket).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
-                                                         HashShape s, int32_t* __restrict__ buckets,
+                                                         const float* __restrict__ rot, HashShape s,
+                                                         int32_t* __restrict__ buckets,
                                                          const int32_t* __restrict__ counts, int n_regions, int cap,
                                                          const int32_t* __restrict__ entries_all, int32_t* n_near_ties) {
   constexpr int kPer = D / 16;
   constexpr int kGroups = 256 / 16;
+  __shared__ double xs[D];
+  __shared__ double red_v[256 / 64];
+  __shared__ int red_b[256 / 64];
   const int sub = threadIdx.x & 15;
   const int group = threadIdx.x >> 4;
+  auto xval = [&](int tok, int k) -> double {
+    if (BF16) return static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[static_cast<size_t>(tok) * D + k]));
+    return static_cast<double>(static_cast<const float*>(qk_raw)[static_cast<size_t>(tok) * D + k]);
+  };
+  auto offer = [&](double& best_v, int& best_b, double p, int c) {
+    const double v = p >= 0.0 ? p : -p;
+    const int b = p >= 0.0 ? c : c + s.half;
+    if (v > best_v || (v == best_v && b < best_b)) { best_v = v; best_b = b; }
+  };
+  auto merge_lanes = [&](double& best_v, int& best_b, int from) {
+    for (int off = from; off > 0; off >>= 1) {
+      const double ov = shfl_xor_d(best_v, off);
+      const int ob = __shfl_xor(best_b, off, 64);
+      if (ov > best_v || (ov == best_v && ob < best_b)) { best_v = ov; best_b = ob; }
+    }
+  };
+  auto store = [&](int tok, int round, int b) {
+    const int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
+    buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = b;
+  };
   int seen = 0;
   for (int region = blockIdx.x; region < n_regions; region += gridDim.x) {
     const int count = counts[region];
@@ -775,29 +863,21 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
       const int tok = entries[3 * static_cast<size_t>(e)];
       const int w1 = entries[3 * static_cast<size_t>(e) + 1];
       const int w2 = entries[3 * static_cast<size_t>(e) + 2];
-      const int round = w1 & 0x7fffffff;
-      const bool full = (w1 & static_cast<int>(0x80000000u)) != 0;
-      const float* R = rt + static_cast<size_t>(round) * s.half * D;
-      auto xval = [&](int k) -> double {
-        if (BF16) return static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[static_cast<size_t>(tok) * D + k]));
-        return static_cast<double>(static_cast<const float*>(qk_raw)[static_cast<size_t>(tok) * D + k]);
-      };
-      // Best candidate as (value, bucket): larger value wins, equal values go to the lower bucket.
+      const int round = w1 & 0x3fffffff;
+      const int kind = (w1 >> 30) & 3;
+      if (kind == kTieFull) continue;   // the same for all 16 lanes of the group
+      const float* Rt = rt + static_cast<size_t>(round) * s.half * D;
       double best_v = -1.0;
       int best_b = 0x7fffffff;
-      auto offer = [&](double p, int c) {
-        double v = p >= 0.0 ? p : -p;
-        int b = p >= 0.0 ? c : c + s.half;   // p == 0: +p (lower bucket) and -p tie; lower wins
-        if (v > best_v || (v == best_v && b < best_b)) { best_v = v; best_b = b; }
-      };
-      if (!full) {
-        const int c1 = w2 & 0xffff, c2 = (w2 >> 16) & 0xffff;
+      const int c1 = w2 & 0xffff;
+      if (kind == kTiePair) {
+        const int c2 = (w2 >> 16) & 0xffff;
         double xv[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) xv[i] = xval(sub * kPer + i);
+        for (int i = 0; i < kPer; ++i) xv[i] = xval(tok, sub * kPer + i);
         double p1 = 0.0, p2 = 0.0;
-        const f32x4* r1 = reinterpret_cast<const f32x4*>(R + static_cast<size_t>(min(c1, s.half - 1)) * D + sub * kPer);
-        const f32x4* r2 = reinterpret_cast<const f32x4*>(R + static_cast<size_t>(min(c2, s.half - 1)) * D + sub * kPer);
+        const f32x4* r1 = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(min(c1, s.half - 1)) * D + sub * kPer);
+        const f32x4* r2 = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(min(c2, s.half - 1)) * D + sub * kPer);
 #pragma unroll
         for (int i = 0; i < kPer / 4; ++i) {
           const f32x4 a = r1[i], b = r2[i];
@@ -812,30 +892,56 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
           p1 += shfl_xor_d(p1, off);
           p2 += shfl_xor_d(p2, off);
         }
-        if (c1 < s.half) offer(p1, c1);
-        if (c2 < s.half && c2 != c1) offer(p2, c2);
+        if (c1 < s.half) offer(best_v, best_b, p1, c1);
+        if (c2 < s.half && c2 != c1) offer(best_v, best_b, p2, c2);
       } else {
-        for (int c = sub; c < s.half; c += 16) {
-          const f32x4* rc = reinterpret_cast<const f32x4*>(R + static_cast<size_t>(c) * D);
+        // c1's group: tile c1 / 32, lane half (c1 / 4) % 2; lane i takes its
+        // projection i, column 32 t + 8 (i / 4) + 4 half + i % 4
+        const int c = 32 * (c1 >> 5) + 8 * (sub >> 2) + 4 * ((c1 >> 2) & 1) + (sub & 3);
+        if (c < s.half) {
+          const f32x4* rc = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(c) * D);
           double p = 0.0;
-#pragma unroll 2
+#pragma unroll 4
           for (int i = 0; i < D / 4; ++i) {
             const f32x4 a = rc[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p += xval(4 * i + j) * static_cast<double>(a[j]);
+            for (int j = 0; j < 4; ++j) p += xval(tok, 4 * i + j) * static_cast<double>(a[j]);
           }
-          offer(p, c);
+          offer(best_v, best_b, p, c);
         }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-          double ov = shfl_xor_d(best_v, off);
-          int ob = __shfl_xor(best_b, off, 64);
-          if (ov > best_v || (ov == best_v && ob < best_b)) { best_v = ov; best_b = ob; }
-        }
+        merge_lanes(best_v, best_b, 8);
       }
-      if (sub == 0) {
-        int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
-        buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = best_b;
+      if (sub == 0) store(tok, round, best_b);
+    }
+    // Full entries, one at a time for the whole workgroup (the entry list and
+    // the loop bounds are the same for every thread).
+    for (int e = 0; e < count; ++e) {
+      const int w1 = entries[3 * static_cast<size_t>(e) + 1];
+      if (((w1 >> 30) & 3) != kTieFull) continue;
+      const int tok = entries[3 * static_cast<size_t>(e)];
+      const int round = w1 & 0x3fffffff;
+      __syncthreads();   // earlier readers of xs, red_v and red_b are done
+      if (threadIdx.x < D) xs[threadIdx.x] = xval(tok, threadIdx.x);
+      __syncthreads();
+      const float* R = rot + static_cast<size_t>(round) * D * s.half;
+      double best_v = -1.0;
+      int best_b = 0x7fffffff;
+      for (int c = threadIdx.x; c < s.half; c += 256) {
+        double p = 0.0;
+#pragma unroll 8
+        for (int k = 0; k < D; ++k) p += xs[k] * static_cast<double>(R[static_cast<size_t>(k) * s.half + c]);
+        offer(best_v, best_b, p, c);
+      }
+      merge_lanes(best_v, best_b, 32);
+      if ((threadIdx.x & 63) == 0) {
+        red_v[threadIdx.x >> 6] = best_v;
+        red_b[threadIdx.x >> 6] = best_b;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int w = 1; w < 256 / 64; ++w)
+          if (red_v[w] > best_v || (red_v[w] == best_v && red_b[w] < best_b)) { best_v = red_v[w]; best_b = red_b[w]; }
+        store(tok, round, best_b);
       }
     }
   }
@@ -937,14 +1043,14 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   const int fix_blocks = std::min(n_regions, 2048);
   if (s.d == 64) {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   }
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();

@@ -23,9 +23,9 @@ HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds
 
 // Byte sizes of the hash scratch regions, in workspace order.
 struct HashScratch {
-  size_t frag_bytes;     // rotation fragments: bf16 R_hi and scaled fp8 R_lo per 32-column tile
+  size_t frag_bytes;     // rotation fragments: bf16 R_hi and block-scaled fp6 R_lo per 32-column tile
   size_t rt_bytes;       // rotations transposed to float32 [round][column][k]
-  size_t bound_bytes;    // per-round column-norm maxima (float bits) and per-tile fp8 scales
+  size_t bound_bytes;    // per-tile column-norm maxima of the error-bound terms (float bits)
   size_t counter_bytes;  // near-tie counter
   size_t list_bytes;     // near-tie list (3 int32 per entry, capacity n_tokens * n_rounds)
   size_t total;

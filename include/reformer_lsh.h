@@ -8,10 +8,10 @@
  *     with random rotations, sorted by bucket, and attention runs only inside
  *     small fixed-size chunks; several hash rounds are combined.
  *   - Key points, LSH attention bullet: h(x) = argmax([xR; -xR]) for a random
- *     matrix R; after sorting, each chunk of m positions attends to itself and
- *     to the chunk before it.
- *   - Key points, Shared-QK bullet: a token is blocked from attending to
- *     itself unless it has no other valid target.
+ *     matrix R; once sorted, the positions are cut into chunks of m and a
+ *     chunk's queries see the keys of that chunk and of the one preceding it.
+ *   - Key points, Shared-QK bullet: a position's own key is excluded from
+ *     its window; it is used only when nothing else is left to attend to.
  *
  * Readings taken where the page is silent (each one is also what the test
  * oracle implements):
@@ -100,12 +100,17 @@ int reformer_lsh_version(void);
  *            top-two gap was too small to trust and were re-decided in
  *            float64 (diagnostic).
  *
- * Projections are computed to float32 accuracy (split-bf16 MFMA for bf16
- * inputs, float32 FMA for float32 inputs).  Any position whose two best
- * float32 candidates are closer than a bound on the float32 error is
- * re-decided between those candidates in float64, so bucket ids agree with
- * exact arithmetic except where the exact top-two gap is itself below the
- * float32 error.
+ * Projections are computed approximately -- bf16 MFMA on R rounded to bf16
+ * plus an fp6 MFMA pass on the rounding residue (bf16 inputs), float32 FMA
+ * (float32 inputs) -- with a rigorous per-token bound tau on the error of a
+ * gap between two projections (Cauchy-Schwarz on the operand residues plus
+ * float32 accumulation plus the key truncation).  A (position, round) whose
+ * leader is within tau of the runner-up is re-decided in float64: between the
+ * two leading candidates when every other candidate is provably more than tau
+ * below the leader, otherwise over all n_buckets/2 columns.  Bucket ids
+ * therefore equal the argmax of exact arithmetic (ties to the lowest bucket)
+ * except where the exact top-two gap is below the float64 rounding of a
+ * d-term dot product (about 1e-13 of |x| max_j |R_j|).
  */
 size_t reformer_lsh_hash_workspace_bytes(int batch, int heads, int seq_len, int d_head,
                                          int n_rounds, int n_buckets);
@@ -265,8 +270,9 @@ rlsh_status_t reformer_lsh_attend_backward_lse(const void* qk, const void* v, rl
 /* -------------------------------------------------------- feed-forward ----
  * Position-wise feed-forward layer applied to chunk_tokens positions at a time
  * ("Reformer: The Efficient Transformer" (research summary), Summary and Key
- * points, reversible layers bullet: chunked feed-forward layers remove the
- * d_ff factor from memory and give numerically identical results):
+ * points, reversible layers bullet: running the feed-forward layers a chunk
+ * of positions at a time takes the d_ff-wide activation out of the memory
+ * bound without changing any result):
  *   out = relu(x W1^T + b1) W2^T + b2   (the pages name no activation; ReLU)
  *
  * x, out   [n_tokens, d_model] bf16 row-major.

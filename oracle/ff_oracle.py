@@ -6,8 +6,9 @@ no code with the HIP library and does not import it.
 
 Source: "Reformer: The Efficient Transformer" (research summary), *Summary*
 (feed-forward layers are processed in chunks) and *Key points*, reversible
-layers bullet (chunking the feed-forward layers removes the d_ff factor from
-memory and gives numerically identical results).  The layer acts on each
+layers bullet (run a chunk of positions at a time, the feed-forward layers
+no longer hold a d_ff-wide activation for the whole sequence, and the results
+do not change).  The layer acts on each
 position independently, so cutting the positions into chunks changes nothing
 but the size of the d_ff-wide intermediate held at one time.
 

@@ -14,10 +14,10 @@ fast.  Sources (page titles as they appear on the pages):
   sorted by bucket, and attention runs inside small fixed-size chunks; several
   hash rounds are used.
 * same page, *Key points*, "LSH attention" bullet: ``h(x) = argmax([xR; -xR])``
-  with a random matrix R; after sorting, each chunk of m positions attends to
-  itself and to the chunk before it.
-* same page, *Key points*, "Shared-QK Transformer" bullet: a token may not
-  attend to itself unless it has no other valid target.
+  with a random matrix R; the sorted positions are cut into chunks of m, and
+  the queries of a chunk see the keys of that chunk and of the preceding one.
+* same page, *Key points*, "Shared-QK Transformer" bullet: a position's own
+  key is excluded, except when nothing else is left for it to attend to.
 * same page, *Key points*, "Number of hash rounds" bullet: more rounds come
   closer to full attention.
 
@@ -40,7 +40,7 @@ with its reason, in the repository's design notes):
   query and key.
 * optional causal mask by original positions: key j is allowed for query i
   only if ``j < i`` (``j == i`` is the self case, handled below).
-* "no other valid target" is decided over all rounds together: a round with
+* whether anything else is left is decided over all rounds together: a round with
   no non-self target contributes nothing (log-normaliser ``-inf``); if no
   round has any, the output is the token's own value vector.
 * rounds are combined with logsumexp weights: ``out_i = sum_r
@@ -163,10 +163,10 @@ def _chunk_len(chunk_len: int, L: int) -> int:
 def chunk_attention_round(x, v, perm, chunk_len: int, causal: bool):
     """One hash round of chunked attention, returned in sequence order.
 
-    "Reformer: The Efficient Transformer", *Key points*: after sorting, each
-    chunk of m positions attends to itself and the chunk before it (LSH
-    attention bullet); queries and keys are the same vectors and a token does
-    not attend to itself (Shared-QK bullet).
+    "Reformer: The Efficient Transformer", *Key points*: the sorted positions
+    form chunks of m whose queries see the keys of their own chunk and of the
+    preceding one (LSH attention bullet); queries and keys are the same
+    vectors and a position's own key is excluded (Shared-QK bullet).
 
     x, v: ``[L, d]``; perm: ``[L]`` (original position at each sorted slot).
     Returns ``(o [L, d], z [L])`` indexed by original position:

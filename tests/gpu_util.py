@@ -62,6 +62,48 @@ def compare_buckets(gpu, x, rotations, n_buckets, rows=None):
     return flips, total
 
 
+def oracle_hash_all(x, rotations, n_buckets, rows_per_task=16384, threads=None):
+    """oracle.lsh_hash on every row of x [B, H, L, d] (float64), in a thread pool.
+
+    The hash is row-independent, so the rows are cut into slices and each
+    slice is one call of the oracle; numpy releases the interpreter lock in
+    the matrix product, the concatenation, argmax and partition, so threads
+    scale.  BLAS itself is held to one thread per call.  Returns buckets and
+    margins, both [B, H, r, L].
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    import threadpoolctl
+
+    B, H, L, _ = x.shape
+    r = 1 if n_buckets == 1 else rotations.shape[0]
+    buckets = np.empty((B, H, r, L), np.int64)
+    margin = np.empty((B, H, r, L), np.float64)
+    tasks = [(b, h, a) for b in range(B) for h in range(H) for a in range(0, L, rows_per_task)]
+
+    def run(t):
+        b, h, a = t
+        e = min(L, a + rows_per_task)
+        ob, om = oracle.lsh_hash(x[b, h, a:e], rotations, n_buckets)
+        buckets[b, h, :, a:e] = ob
+        margin[b, h, :, a:e] = om
+
+    n = threads or min(16, len(os.sched_getaffinity(0)))
+    with threadpoolctl.threadpool_limits(1):
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(run, tasks))
+    return buckets, margin
+
+
+def bucket_parity(gpu, want, margin):
+    """Every id compared: returns (flips, near_ties, bad) where flips counts
+    differing ids, near_ties the (position, round) pairs whose exact top-two
+    gap is below NEAR_TIE, and bad the flips outside near-ties (must be 0)."""
+    mism = gpu != want
+    bad = mism & (margin >= NEAR_TIE)
+    return int(mism.sum()), int((margin < NEAR_TIE).sum()), int(bad.sum())
+
+
 def oracle_perm(buckets):
     """Stable sort of every (b, h, round) of the given bucket ids with the oracle."""
     B, H, r, L = buckets.shape

@@ -1,5 +1,5 @@
 """Chunked feed-forward on the GPU: against the float64 oracle, and bit-equal
-results for every chunk size ("numerically identical")."""
+results for every chunk size (chunking must not change any result)."""
 import numpy as np
 import pytest
 

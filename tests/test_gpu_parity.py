@@ -82,8 +82,8 @@ def test_hash_zero_and_duplicate_vectors(nat):
 @pytest.mark.parametrize("rot_scale", [2.0 ** -40, 1.0, 2.0 ** 40])
 def test_hash_wide_dynamic_range(nat, rot_scale):
     """Features whose magnitudes span about 10^8 inside one 32-feature block and
-    rotations scaled far from 1: the per-block fp8 scales of x and the per-tile
-    scale of the rotation's low part must still give exact bucket ids."""
+    rotations scaled far from 1: the per-block fp6 scales of x and of the
+    rotation's low part must still give exact bucket ids."""
     import torch
 
     rng = np.random.default_rng(11)
@@ -176,6 +176,97 @@ def test_hash_extreme_scales(nat, x_exp, rot_exp, dtype):
     _say(f"[hash-scale] x 2^{x_exp} R 2^{rot_exp} {dtype}: re-decided {n_ties} of {B * H * L * r}")
     if x_exp <= -100 or rot_exp <= -70:
         assert n_ties == B * H * L * r
+
+
+def _in_bin_case(layout, dtype, L=512, seed=3):
+    """Tokens whose three leading rotation columns share one key truncation bin.
+
+    8192 buckets (4096 columns, the 512K-token shape's count): a column's key
+    keeps 11 mantissa bits, so projections 30, 30 + s, 30 + 2s, 30 + 3s with
+    s = 2^-10 truncate alike and keys rank them by candidate code.  The exact
+    winner (30 + 3s) is given the lowest code of the three, so the top two
+    keys are the two losers.  Exact top-two gaps are s times the token's scale
+    (at least 2^-13), far above 1e-5: every id must match the oracle.
+
+    layout "groups": the three columns in different column tiles (the winner
+    is the third key); "same_group": the three in one lane's 16 projections of
+    one tile (the winner is not even among that group's top two); "mixed": the
+    two losers in one group, the winner in another (the top two keys share a
+    group and the third is within the bound).  Half the
+    tokens have that structure at scales 2^-3..2^3 and either sign, the rest
+    are iid normal; other columns project to at most 0.8 times the leader."""
+    import torch
+
+    g = np.random.default_rng(seed)
+    d, nb = 64, 8192
+    half = nb // 2
+    cols = {"groups": (0, 160, 288), "same_group": (96, 97, 98), "mixed": (0, 160, 161)}[layout]
+    rot = g.standard_normal((1, d, half)).astype(np.float32)
+    rot[0, 0, :] = g.uniform(-0.8, 0.8, half).astype(np.float32)
+    rot[0, 1, :] = g.standard_normal(half).astype(np.float32)
+    for k, c in zip((3.0, 2.0, 1.0), cols):   # winner, runner-up, third
+        rot[0, 0, c] = 1.0
+        rot[0, 1, c] = k
+    x = g.standard_normal((1, 1, L, d))
+    special = np.arange(L) % 2 == 0
+    scale = np.ldexp(np.where(g.random(L) < 0.5, -1.0, 1.0), g.integers(-3, 4, L))
+    x[0, 0, special] = 0.0
+    x[0, 0, special, 0] = 30.0 * scale[special]
+    x[0, 0, special, 1] = 2.0 ** -10 * scale[special]
+    x32 = x.astype(np.float32)
+    if dtype == "bf16":
+        bits = W.f32_to_bf16_bits(x32)
+        qk = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        xe = W.bf16_bits_to_f32(bits).astype(np.float64)
+    else:
+        qk = torch.from_numpy(x32).cuda()
+        xe = x32.astype(np.float64)
+    return qk, torch.from_numpy(rot).cuda(), rot, xe, nb, special, cols
+
+
+@pytest.mark.parametrize("layout,dtype", [("groups", "bf16"), ("same_group", "bf16"), ("mixed", "bf16"),
+                                          ("groups", "f32"), ("same_group", "f32"), ("mixed", "f32")])
+def test_hash_third_candidate_in_bin(nat, layout, dtype):
+    """Three candidates in one key truncation bin with the winner ranked third
+    by key: the kernel must not re-decide between the top two keys only."""
+    qk, rot_d, rot, x, nb, special, cols = _in_bin_case(layout, dtype)
+    b, ties = nat.lsh_hash(qk, rot_d, nb, return_near_ties=True)
+    g = host(b)[0, 0]
+    ob, om = oracle.lsh_hash(x[0, 0], rot, nb)
+    assert np.all(om[:, special] >= 2.0 ** -14)
+    mism = g != ob
+    _say(f"[hash-bin] {layout} {dtype}: mismatches {int(mism.sum())}, re-decided {int(ties.item())}")
+    assert not mism.any(), f"gpu {g[mism][:8]} oracle {ob[mism][:8]} margins {om[mism][:8]}"
+    want = np.where(x[0, 0, special, 0] > 0, cols[0], cols[0] + nb // 2)
+    assert np.array_equal(g[0, special], want)
+    assert int(ties.item()) >= int(special.sum())
+
+
+# (round, position) pairs of the 512K-token workload (batch 0, head 0) whose
+# exact winner a top-two-only re-decision misses: three candidates share the
+# leader's key truncation bin there (exact top-two margins 2e-4 to 2.8e-3).
+HALF_MILLION_ROWS = ((0, 183926), (0, 423027), (0, 453736), (1, 241626))
+
+
+def test_hash_half_million_third_candidate_rows(nat):
+    """Those rows hashed on their own (the same features and rotations, so the
+    same approximate projections per row) must give the oracle's buckets."""
+    import torch
+
+    inp = W.make_inputs("half_million")
+    w = inp.workload
+    pos = np.array(sorted({p for _, p in HALF_MILLION_ROWS}))
+    rounds = 1 + max(r for r, _ in HALF_MILLION_ROWS)
+    sel = np.ascontiguousarray(inp.qk_bits[0:1, 0:1, pos])
+    qk = torch.from_numpy(sel.view(np.int16)).view(torch.bfloat16).cuda()
+    rot = np.ascontiguousarray(inp.rotations[:rounds])
+    b = host(nat.lsh_hash(qk, torch.from_numpy(rot).cuda(), w.n_buckets))[0, 0]
+    ob, om = oracle.lsh_hash(inp.qk[0, 0, pos].astype(np.float64), rot, w.n_buckets)
+    for r, p in HALF_MILLION_ROWS:
+        i = int(np.searchsorted(pos, p))
+        _say(f"[hash-512k] round {r} position {p}: gpu {b[r, i]} oracle {ob[r, i]} margin {om[r, i]:.3e}")
+        assert om[r, i] >= 1e-5 and b[r, i] == ob[r, i]
+    assert np.array_equal(b, ob) or np.all(om[b != ob] < 1e-5)
 
 
 def test_hash_one_bucket(nat):

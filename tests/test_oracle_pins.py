@@ -171,6 +171,39 @@ def test_forward_matches_pure_python_brute_force(chunk_len, causal, n_rounds):
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
+def test_batched_wrapper_matches_brute_force_per_slice():
+    """oracle.lsh_attention over [B, H, L, d]: every (batch, head) slice has
+    its own inputs, and each slice's output, bucket ids and margins must be
+    that slice's pure-Python brute force / exact hash -- a swapped batch and
+    head index, or a slice written to the wrong place, fails here."""
+    g = np.random.default_rng(77)
+    B, H, L, d, nb, r, m = 2, 3, 12, 4, 4, 2, 4
+    qk = g.standard_normal((B, H, L, d))
+    v = g.standard_normal((B, H, L, 3))
+    R = g.standard_normal((r, d, nb // 2))
+    res = oracle.lsh_attention(qk, v, R, nb, m, True)
+    assert res["out"].shape == (B, H, L, 3) and res["buckets"].shape == (B, H, r, L)
+    for b in range(B):
+        for h in range(H):
+            want = _brute_force_forward(qk[b, h].tolist(), v[b, h].tolist(), R, nb, m, True)
+            np.testing.assert_allclose(res["out"][b, h], want, rtol=0, atol=1e-12)
+            for rho in range(r):
+                for i in range(L):
+                    best, gap = oracle.exact_projection_margin(qk[b, h, i], R[rho], nb)
+                    assert res["buckets"][b, h, rho, i] == best
+                    assert abs(res["margin"][b, h, rho, i] - float(gap)) <= 1e-12
+    # supplied bucket ids are used per slice: the slices' own ids give the same output
+    again = oracle.lsh_attention(qk, v, R, nb, m, True, buckets=res["buckets"])
+    np.testing.assert_array_equal(again["out"], res["out"])
+    # swapping two slices' inputs swaps their outputs
+    qk2, v2 = qk.copy(), v.copy()
+    qk2[0, 1], qk2[1, 2] = qk[1, 2], qk[0, 1]
+    v2[0, 1], v2[1, 2] = v[1, 2], v[0, 1]
+    swapped = oracle.lsh_attention(qk2, v2, R, nb, m, True)["out"]
+    np.testing.assert_array_equal(swapped[0, 1], res["out"][1, 2])
+    np.testing.assert_array_equal(swapped[1, 2], res["out"][0, 1])
+
+
 # ----------------------------------------------- hand-worked attention ----
 
 @pytest.mark.parametrize("case", _golden()["attention"]["cases"], ids=lambda c: c["note"][:40])
