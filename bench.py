@@ -453,18 +453,26 @@ def profile_stage(args, st, w):
 
 
 def accuracy_sweep(args):
-    """Error of LSH attention against full attention as rounds and buckets vary.
+    """Error and cost of LSH attention against full attention as rounds and
+    buckets vary ("Reformer: The Efficient Transformer", Key points, Number of
+    hash rounds bullet: more rounds come closer to full attention and cost
+    more).
 
-    Both sides run in this library on the GPU: full shared-QK attention is the
-    same pipeline with one bucket and one chunk spanning the sequence (every
-    key visible, self masked unless it is the only key), whose agreement with
-    the float64 oracle the parity tests check.  Inputs: the small causal shape
-    (batch 2, 4 heads, L = 4096, d = 64, chunks of 64, float32) with iid normal
-    and with clustered (mixture) shared vectors, the latter also scaled by 3
-    (peaked attention); v iid normal.  Reported: the relative Frobenius error
-    ||out - full|| / ||full|| over all heads.  Diffuse full attention averages
-    thousands of rows of v, so its norm is small and the relative error of any
-    128-key window exceeds 1 there.
+    Error: both sides run in this library on the GPU; full shared-QK attention
+    is the same pipeline with one bucket and one chunk spanning the sequence
+    (every key visible, self masked unless it is the only key), which the GPU
+    tests check against the float64 oracle at this very shape.  Inputs: the
+    small causal shape (batch 2, 4 heads, L = 4096, d = 64, chunks of 64,
+    float32) with iid normal, clustered (mixture) and position-smooth (AR(1),
+    rho = 0.9) shared vectors, the mixture also scaled by 3 (peaked
+    attention); v iid normal.  Reported: the relative Frobenius error
+    ||out - full|| / ||full|| over all heads, and the GPU time per forward at
+    that shape.  Diffuse full attention averages thousands of rows of v, so
+    its norm is small and the relative error of any 128-key window exceeds 1.
+
+    Cost: milliseconds per forward for every (rounds, buckets) cell at the
+    64K-token text shape (batch 1, 8 heads, d = 128, chunks of 64, causal,
+    bf16, mixture input), where the work is large enough to show it.
     """
     import dataclasses
 
@@ -484,7 +492,7 @@ def accuracy_sweep(args):
     # (label, generator kind, factor on qk): the mixture scaled by 3 makes the
     # attention peaked (same-centre scores ~ 81/sqrt(d)) instead of diffuse.
     for label, kind, qk_scale in (("normal", "normal", 1.0), ("mixture", "mixture", 1.0),
-                                  ("mixture_x3", "mixture", 3.0)):
+                                  ("mixture_x3", "mixture", 3.0), ("ar1", "ar1", 1.0)):
         w0 = dataclasses.replace(base, qk_kind=kind, name=f"sweep_{kind}")
         ref_in = W.make_inputs(dataclasses.replace(w0, n_buckets=1, n_rounds=1))
         qk = torch.from_numpy((ref_in.qk * np.float32(qk_scale)).astype(np.float32)).cuda()
@@ -497,13 +505,36 @@ def accuracy_sweep(args):
                 rot = torch.from_numpy(inp.rotations).cuda()
                 out = nat.attention(qk, v, rot, b, w0.chunk_len, w0.causal, n_rounds=r).double()
                 err = float(torch.linalg.vector_norm(out - full)) / fnorm
-                rows.append({"qk": label, "n_buckets": b, "n_rounds": r, "rel_err": round(err, 5)})
-                log(args, f"[sweep] {label:10s} b={b:4d} r={r}: {err:.4f}")
+                ws = torch.empty(nat.workspace_bytes(base.batch, base.heads, base.seq_len, base.d_head, r, b,
+                                                     base.chunk_len, torch.float32), dtype=torch.uint8, device="cuda")
+                o = torch.empty_like(v)
+                ms = time_calls(lambda: nat.attention(qk, v, rot, b, w0.chunk_len, w0.causal, n_rounds=r,  # noqa: B023
+                                                      workspace=ws, out=o), 10, 2)
+                rows.append({"qk": label, "n_buckets": b, "n_rounds": r, "rel_err": round(err, 5), "ms": round(ms, 4)})
+                log(args, f"[sweep] {label:10s} b={b:4d} r={r}: {err:.4f}  {ms:.3f} ms")
+    # cost at the 64K-token text shape
+    text = W.WORKLOADS["text_64k"]
+    t_in = W.make_inputs(text)
+    qk = torch.from_numpy(t_in.qk_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    v = torch.from_numpy(t_in.v_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    cost = []
+    for b in [64, 256, 1024, 4096]:
+        for r in rounds:
+            g = np.random.default_rng(np.random.SeedSequence([20200104, 990, b, r]))
+            rot = torch.from_numpy(g.standard_normal((r, text.d_head, b // 2), dtype=np.float32)).cuda()
+            ws = torch.empty(nat.workspace_bytes(text.batch, text.heads, text.seq_len, text.d_head, r, b,
+                                                 text.chunk_len, torch.bfloat16), dtype=torch.uint8, device="cuda")
+            o = torch.empty_like(v)
+            ms = time_calls(lambda: nat.attention(qk, v, rot, b, text.chunk_len, text.causal, n_rounds=r,  # noqa: B023
+                                                  workspace=ws, out=o), 10, 3)
+            cost.append({"n_buckets": b, "n_rounds": r, "ms": round(ms, 4)})
+            log(args, f"[sweep-cost] text_64k b={b:5d} r={r}: {ms:.3f} ms")
+            del ws, o
     print(json.dumps({"accuracy_sweep": rows, "shape": {"batch": base.batch, "heads": base.heads,
                       "seq_len": base.seq_len, "d_head": base.d_head, "chunk_len": base.chunk_len,
                       "causal": base.causal, "dtype": "f32"},
-                      "reference": "full shared-QK attention (one bucket, one chunk) in the same library"}),
-          flush=True)
+                      "reference": "full shared-QK attention (one bucket, one chunk) in the same library",
+                      "cost_text_64k": cost}), flush=True)
 
 
 def local_bench(args):

@@ -21,11 +21,13 @@
 //     the sign cleared and a candidate code in the low mantissa bits.  A
 //     running top-two of keys per lane takes a med3, a max and a max3 per two
 //     values; once per tile the lane's top two are merged into a running top
-//     three.  The sign is left out of the keys: a running maximum of the raw
-//     float bits as signed integers (a max3 per two values) tells at the end
-//     of the round whether the winner is positive -- it is exactly when that
-//     maximum reaches the winner's magnitude.  The two lanes sharing a token
-//     merge once per round.
+//     three.  The sign is left out of the keys: with many column tiles per
+//     round, the leader's projection is recomputed at the end of the round
+//     from x . R_hi alone (v_dot2 on the bf16 operands the lane already
+//     holds), whose error bound shows its sign is that of the exact
+//     projection (else the position is re-decided); with few, a running
+//     maximum of the raw bits as signed integers gives it.  The two lanes
+//     sharing a token merge once per round.
 //   * The leading keys give the two leading candidates and their gap.  When the
 //     gap is below twice a bound on the error of one projection (plus the key
 //     truncation), the (position, round) is queued and a fix-up kernel
@@ -159,26 +161,23 @@ __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int roun
 //   else m1 - m3 > tau, two groups -> float64 re-decision between the top two;
 //   else m1 - m3 > tau, one group  -> float64 re-decision over G's columns;
 //   else                           -> float64 re-decision over all columns
-// (also when even the leader's magnitude is within tau, e.g. x = 0).  smax is
-// the largest raw projection bit pattern as a signed integer (the largest
-// positive projection, if any): the winner is positive exactly when smax
-// reaches its truncated magnitude.  Were the winner negative while a positive
-// projection reached that magnitude, the two would share a truncated
-// magnitude, so the gap would be zero and the fix-up would decide.
-__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, uint32_t k3, bool same_group, int32_t smax,
-                                                 int col1, int col2, float tau_x, int code_bits, int half, int tok,
-                                                 int seq_len, int n_rounds, int round, int32_t* buckets,
+// (also when even the leader's magnitude is within tau, e.g. x = 0, or when
+// the caller cannot vouch for the sign of the leader's projection: sign_ok).
+// positive is the sign of the leader's projection, which picks bucket c1 or
+// c1 + b/2.
+__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, uint32_t k3, bool same_group, bool positive,
+                                                 bool sign_ok, int col1, int col2, float tau_x, int code_bits, int half,
+                                                 int tok, int seq_len, int n_rounds, int round, int32_t* buckets,
                                                  NearTieList lst) {
   const uint32_t code_mask = (1u << code_bits) - 1u;
   const float m1 = key_magnitude(k1, code_mask);
   const float m2 = key_magnitude(k2, code_mask);
   const float m3 = key_magnitude(k3, code_mask);
   const float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
-  const bool positive = smax >= static_cast<int32_t>(k1 & ~code_mask);
   const int bucket = col1 + (positive ? 0 : half);
   const int bh = tok / seq_len, pos = tok - bh * seq_len;
   buckets[(static_cast<size_t>(bh) * n_rounds + round) * seq_len + pos] = bucket;
-  const bool tiny = !(m1 > tau);
+  const bool tiny = !(m1 > tau) || !sign_ok;
   const bool near = !((m1 - m2) > tau);
   const bool third_far = (m1 - m3) > tau;
   if (tiny || near) {
@@ -303,7 +302,7 @@ template <int D, bool FRAG>
 __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_rounds,
                                                            int n_ctiles, u32x4* __restrict__ frag,
                                                            float* __restrict__ rt, uint32_t* __restrict__ bound_bits,
-                                                           int32_t* n_near_ties) {
+                                                           int32_t* n_near_ties, int32_t* __restrict__ full_count) {
   using FT = FragTile<D>;
   constexpr int kGroups = 8;               // k-ranges per column
   constexpr int kPerG = D / kGroups;       // 8 or 16 values
@@ -406,6 +405,8 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
     max32_to(c < half ? norm_bits_up(sum) : 0u, bound_bits + kBoundCmax * term + slot);
     // the caller's near-tie total starts from zero (the fix-up kernel adds to it)
     if (threadIdx.x == 0 && t == 0 && r == 0 && n_near_ties != nullptr) *n_near_ties = 0;
+    // this round's list of full re-decisions starts empty (the fix-up kernel appends)
+    if (threadIdx.x == 0 && t == 0) full_count[r] = 0;
     if (FRAG) {
       double sr = 0.0, sl = 0.0;
 #pragma unroll
@@ -436,6 +437,10 @@ __device__ __forceinline__ void lds_dma16(const u32x4* g, u32x4* l) {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 typedef float f32x16v __attribute__((ext_vector_type(16)));
+// Operand type of v_dot2_f32_bf16.  It must be a clang extended vector: with
+// the generic __vector_size__ bf16 pair, element e of a u32x4 bit-cast into
+// the builtin's argument compiles to element 0 for every e.
+typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
 typedef float f32x32v __attribute__((ext_vector_type(32)));
 typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 
@@ -513,7 +518,17 @@ __device__ __forceinline__ i32x8 x_to_fp6(const uint16_t* __restrict__ xrow, boo
                static_cast<int>(w[3]), static_cast<int>(w[4]), static_cast<int>(w[5]), 0, 0};
 }
 
-template <int D>
+// The leader's sign: with SIGN_AT_END, recomputed at the end of each round
+// from x . R_hi of the leading column (no per-value work, but a dependent
+// global load per round end, worth it when rounds span many tiles); else a
+// running maximum of the raw projection bits as signed integers (a max3 per
+// two values): the leader is positive exactly when it reaches the leader's
+// truncated magnitude (were the leader negative while a positive projection
+// reached that magnitude, the two would share a truncated magnitude, so the
+// gap would be zero and the fix-up would decide).
+constexpr int kSignAtEndTiles = 32;   // column tiles per round from which SIGN_AT_END is used
+
+template <int D, bool SIGN_AT_END>
 __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kernel(
     const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ bound_bits,
     HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
@@ -644,14 +659,16 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
       const uint32_t a1 = make_key(acc[st][0], keep_mask, 0u);
       const uint32_t a2 = make_key(acc[st][1], keep_mask, 1u);
       uint32_t t1 = max(a1, a2), t2 = min(a1, a2);
-      int32_t sm = max(max(smax[st], __float_as_int(acc[st][0])), __float_as_int(acc[st][1]));
 #pragma unroll
-      for (int i = 2; i < 16; i += 2) {
+      for (int i = 2; i < 16; i += 2)
         top2_push2(t1, t2, make_key(acc[st][i], keep_mask, static_cast<uint32_t>(i)),
                    make_key(acc[st][i + 1], keep_mask, static_cast<uint32_t>(i + 1)));
-        sm = max(max(sm, __float_as_int(acc[st][i])), __float_as_int(acc[st][i + 1]));
+      if (!SIGN_AT_END) {
+        int32_t sm = smax[st];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) sm = max(max(sm, __float_as_int(acc[st][i])), __float_as_int(acc[st][i + 1]));
+        smax[st] = sm;
       }
-      smax[st] = sm;
       top3_merge2(k1[st], k2[st], k3[st], t1 | tile_code, t2 | tile_code);
     }
   };
@@ -669,26 +686,60 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
       rho1 = round_bound(bound_bits, kBoundRes, s.n_rounds, s.n_ctiles, round);
       rho2 = round_bound(bound_bits, kBoundLo, s.n_rounds, s.n_ctiles, round);
     }
+    auto col_of = [](uint32_t c) {
+      uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
+      return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
+    };
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
       const uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32), o3 = shfl_xor_u(k3[st], 32);
-      top3_merge3(k1[st], k2[st], k3[st], o1, o2, o3);
-      const int32_t sm = max(smax[st], static_cast<int32_t>(shfl_xor_u(static_cast<uint32_t>(smax[st]), 32)));
+      top3_merge3(k1[st], k2[st], k3[st], o1, o2, o3);   // the same on both lanes of the token
+      const uint32_t c1 = k1[st] & code_mask, c2 = k2[st] & code_mask;
+      const int col1 = col_of(c1);
+      float sd = 0.0f;
+      if (SIGN_AT_END) {
+        // Sign of the leader's projection from x . R_hi alone: the A fragment
+        // of lane col1 % 32 + 32 half_sel of its tile holds R_hi of column
+        // col1 for exactly the features of this lane's B operands, so each
+        // lane of the token adds up its half.
+        const u32x4* fr = frag + (static_cast<size_t>(round) * s.n_ctiles + (col1 >> 5)) * kTileVec + (col1 & 31) +
+                          32 * half_sel;
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+          const u32x4 a = fr[ks * 64];
+          const u32x4 b = __builtin_bit_cast(u32x4, xf[st][ks]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t ae = a[e], be = b[e];
+            sd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, ae), __builtin_bit_cast(bf16x2e, be), sd,
+                                                 false);
+          }
+        }
+        sd += shfl_xor_f(sd, 32);
+      }
+      const int32_t sm = SIGN_AT_END ? 0 : max(smax[st], static_cast<int32_t>(shfl_xor_u(static_cast<uint32_t>(smax[st]), 32)));
       int tok = tok_base + 32 * st + lane;
       if (lane < 32 && tok < s.n_tokens) {
         const volatile float* xnv = reinterpret_cast<const volatile float*>(&xnorm[st][threadIdx.x]);
         const float2 xn = make_float2(xnv[0], xnv[1]);
-        uint32_t c1 = k1[st] & code_mask, c2 = k2[st] & code_mask;
-        auto col_of = [](uint32_t c) {
-          uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
-          return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
-        };
+        const float tau_x = split_gap_bound(xn.x, xn.y, cmax, rho1, rho2);
+        bool positive = true, sign_ok = true;
+        if (SIGN_AT_END) {
+          // |p - x.R_hi| <= |x| |R_lo| <= |x| (rho1 + rho2), plus float32
+          // accumulation of exact bf16 products; the leader's exact |p| is at
+          // least m1 - tau_x / 2, so its sign is that of sd when m1 exceeds
+          // tau_x plus that error.
+          const float e_sign = (xn.x * (rho1 + rho2) + kAccRel * xn.x * cmax) * (1.0f + 1.0f / 1024.0f);
+          positive = sd > 0.0f;
+          sign_ok = key_magnitude(k1[st], code_mask) > tau_x + e_sign;
+        } else {
+          positive = sm >= static_cast<int32_t>(k1[st] & ~code_mask);
+        }
         // a group is one lane's 16 projections of one tile: code >> 4 is
         // (tile, lane half)
         const bool same_group = ((c1 ^ c2) >> 4) == 0u;
-        decide_and_store(k1[st], k2[st], k3[st], same_group, sm, col_of(c1), col_of(c2),
-                         split_gap_bound(xn.x, xn.y, cmax, rho1, rho2), s.code_bits, s.half, tok, s.seq_len,
-                         s.n_rounds, round, buckets, lst);
+        decide_and_store(k1[st], k2[st], k3[st], same_group, positive, sign_ok, col1, col_of(c2), tau_x, s.code_bits,
+                         s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
       }
       k1[st] = 0u;
       k2[st] = 0u;
@@ -799,7 +850,13 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
     const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
     if (live) {
       int c1 = static_cast<int>(k1 & code_mask), c2 = static_cast<int>(k2 & code_mask);
-      decide_and_store(k1, k2, k3, false, smax, c1, c2, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
+      // the leader is positive exactly when the largest raw bit pattern as a
+      // signed integer (the largest positive projection, if any) reaches its
+      // truncated magnitude; were it negative while a positive projection
+      // reached that magnitude, the two would share a truncated magnitude, so
+      // the gap would be zero and the fix-up would decide
+      const bool positive = smax >= static_cast<int32_t>(k1 & ~code_mask);
+      decide_and_store(k1, k2, k3, false, positive, true, c1, c2, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
                        s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
@@ -815,23 +872,19 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
 //    holds features [i*D/16, (i+1)*D/16) and the two column dot products are
 //    summed across the 16 lanes.  Group: lane i scores column i of the group
 //    (a whole dot product, the column read from the transposed copy).
-//  * full entries take the whole workgroup: x staged in LDS as float64,
-//    thread t scores columns t, t + 256, ... with the rotations in their
-//    original [k][column] layout (a wavefront reads 64 consecutive floats per
-//    feature), then a workgroup reduction.
+//  * full entries are appended to their round's list for hash_full_kernel.
 // Best candidate as (value, bucket): the larger value wins, equal values go
 // to the lower bucket; p == 0 counts as +p (the lower bucket).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
-                                                         const float* __restrict__ rot, HashShape s,
+                                                         HashShape s,
                                                          int32_t* __restrict__ buckets,
                                                          const int32_t* __restrict__ counts, int n_regions, int cap,
-                                                         const int32_t* __restrict__ entries_all, int32_t* n_near_ties) {
+                                                         const int32_t* __restrict__ entries_all, int32_t* n_near_ties,
+                                                         int32_t* __restrict__ full_count,
+                                                         int32_t* __restrict__ full_list) {
   constexpr int kPer = D / 16;
   constexpr int kGroups = 256 / 16;
-  __shared__ double xs[D];
-  __shared__ double red_v[256 / 64];
-  __shared__ int red_b[256 / 64];
   const int sub = threadIdx.x & 15;
   const int group = threadIdx.x >> 4;
   auto xval = [&](int tok, int k) -> double {
@@ -865,7 +918,10 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
       const int w2 = entries[3 * static_cast<size_t>(e) + 2];
       const int round = w1 & 0x3fffffff;
       const int kind = (w1 >> 30) & 3;
-      if (kind == kTieFull) continue;   // the same for all 16 lanes of the group
+      if (kind == kTieFull) {   // the same for all 16 lanes of the group
+        if (sub == 0) full_list[static_cast<size_t>(round) * s.n_tokens + atomicAdd(&full_count[round], 1)] = tok;
+        continue;
+      }
       const float* Rt = rt + static_cast<size_t>(round) * s.half * D;
       double best_v = -1.0;
       int best_b = 0x7fffffff;
@@ -913,39 +969,108 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
       }
       if (sub == 0) store(tok, round, best_b);
     }
-    // Full entries, one at a time for the whole workgroup (the entry list and
-    // the loop bounds are the same for every thread).
-    for (int e = 0; e < count; ++e) {
-      const int w1 = entries[3 * static_cast<size_t>(e) + 1];
-      if (((w1 >> 30) & 3) != kTieFull) continue;
-      const int tok = entries[3 * static_cast<size_t>(e)];
-      const int round = w1 & 0x3fffffff;
-      __syncthreads();   // earlier readers of xs, red_v and red_b are done
-      if (threadIdx.x < D) xs[threadIdx.x] = xval(tok, threadIdx.x);
-      __syncthreads();
-      const float* R = rot + static_cast<size_t>(round) * D * s.half;
-      double best_v = -1.0;
-      int best_b = 0x7fffffff;
-      for (int c = threadIdx.x; c < s.half; c += 256) {
-        double p = 0.0;
+  }
+  if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
+}
+
+// Full re-decisions, batched: a workgroup takes kFullBatch positions of one
+// round's list and stages their features in LDS as float64.  Rotation columns
+// go through LDS in tiles of 64 (all of a tile's loads in flight, the next
+// tile loaded into registers while the current one is scored; R's original
+// [k][column] layout, so every wavefront load reads 256 contiguous bytes).
+// Wavefront w scores positions 2w and 2w + 1 against the tile's 64 columns,
+// one column per lane, and keeps each position's best over the columns it
+// has seen; a wavefront reduction gives the bucket.
+constexpr int kFullBatch = 8;
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void hash_full_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rot,
+                                                        HashShape s, int32_t* __restrict__ buckets,
+                                                        const int32_t* __restrict__ full_count,
+                                                        const int32_t* __restrict__ full_list) {
+  constexpr int E = kFullBatch;
+  constexpr int kCols = 64;
+  constexpr int kPer = D * kCols / 256;   // tile entries loaded per thread
+  static_assert(E == 2 * (256 / 64), "two positions per wavefront");
+  __shared__ double xs[D][E];
+  __shared__ float tile[2][D][kCols];
+  __shared__ int toks[E];
+  const int round = blockIdx.y;
+  const int count = full_count[round];
+  const int32_t* list = full_list + static_cast<size_t>(round) * s.n_tokens;
+  const float* R = rot + static_cast<size_t>(round) * D * s.half;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_tiles = (s.half + kCols - 1) / kCols;
+  // tile entry i of this thread: feature (threadIdx.x + 256 i) / 64, column (threadIdx.x + 256 i) % 64 = lane
+  auto load_tile = [&](float (&v)[kPer], int t) {
+    const int c = t * kCols + lane;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int k = (threadIdx.x >> 6) + 4 * i;
+      v[i] = c < s.half ? R[static_cast<size_t>(k) * s.half + c] : 0.0f;
+    }
+  };
+  for (int base = blockIdx.x * E; base < count; base += gridDim.x * E) {
+    const int ne = min(E, count - base);
+    __syncthreads();   // earlier readers of toks, xs and tile are done
+    if (threadIdx.x < E) toks[threadIdx.x] = threadIdx.x < ne ? list[base + threadIdx.x] : -1;
+    __syncthreads();
+    for (int u = threadIdx.x; u < E * D; u += 256) {
+      const int e = u / D, k = u - e * D;
+      const int tok = toks[e];
+      double xv = 0.0;
+      if (tok >= 0) {
+        const size_t at = static_cast<size_t>(tok) * D + k;
+        xv = BF16 ? static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[at]))
+                  : static_cast<double>(static_cast<const float*>(qk_raw)[at]);
+      }
+      xs[k][e] = xv;
+    }
+    float v[kPer];
+    load_tile(v, 0);
+    double bv0 = -1.0, bv1 = -1.0;
+    int bb0 = 0x7fffffff, bb1 = 0x7fffffff;
+    const int e0 = 2 * wave, e1 = 2 * wave + 1;
+    for (int t = 0; t < n_tiles; ++t) {
+      float (&cur)[D][kCols] = tile[t & 1];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) cur[(threadIdx.x >> 6) + 4 * i][lane] = v[i];
+      __syncthreads();   // the tile (and, first time round, xs) is in LDS
+      if (t + 1 < n_tiles) load_tile(v, t + 1);
+      double p0 = 0.0, p1 = 0.0;
 #pragma unroll 8
-        for (int k = 0; k < D; ++k) p += xs[k] * static_cast<double>(R[static_cast<size_t>(k) * s.half + c]);
-        offer(best_v, best_b, p, c);
+      for (int k = 0; k < D; ++k) {
+        const double r = static_cast<double>(cur[k][lane]);
+        p0 += xs[k][e0] * r;
+        p1 += xs[k][e1] * r;
       }
-      merge_lanes(best_v, best_b, 32);
-      if ((threadIdx.x & 63) == 0) {
-        red_v[threadIdx.x >> 6] = best_v;
-        red_b[threadIdx.x >> 6] = best_b;
+      const int c = t * kCols + lane;
+      if (c < s.half) {
+        const double a0 = p0 >= 0.0 ? p0 : -p0, a1 = p1 >= 0.0 ? p1 : -p1;
+        const int b0 = p0 >= 0.0 ? c : c + s.half, b1 = p1 >= 0.0 ? c : c + s.half;
+        if (a0 > bv0 || (a0 == bv0 && b0 < bb0)) { bv0 = a0; bb0 = b0; }
+        if (a1 > bv1 || (a1 == bv1 && b1 < bb1)) { bv1 = a1; bb1 = b1; }
       }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        for (int w = 1; w < 256 / 64; ++w)
-          if (red_v[w] > best_v || (red_v[w] == best_v && red_b[w] < best_b)) { best_v = red_v[w]; best_b = red_b[w]; }
-        store(tok, round, best_b);
+      // the other buffer is rewritten next step only after this barrier
+      // has been passed by every wavefront, which the next step's barrier
+      // orders (two buffers)
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const double o0 = shfl_xor_d(bv0, off), o1 = shfl_xor_d(bv1, off);
+      const int c0 = __shfl_xor(bb0, off, 64), c1 = __shfl_xor(bb1, off, 64);
+      if (o0 > bv0 || (o0 == bv0 && c0 < bb0)) { bv0 = o0; bb0 = c0; }
+      if (o1 > bv1 || (o1 == bv1 && c1 < bb1)) { bv1 = o1; bb1 = c1; }
+    }
+    if (lane == 0) {
+      for (int j = 0; j < 2; ++j) {
+        const int e = 2 * wave + j;
+        if (e >= ne) continue;
+        const int tok = toks[e];
+        const int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
+        buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = j == 0 ? bb0 : bb1;
       }
     }
   }
-  if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
 }
 
 __global__ void fill_zero_kernel(int32_t* p, size_t n) {
@@ -986,7 +1111,11 @@ HashScratch hash_scratch(const HashShape& s) {
   const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
   h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
   h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
-  h.total = h.frag_bytes + h.rt_bytes + h.bound_bytes + h.counter_bytes + h.list_bytes;
+  // per round: a counter and up to n_tokens positions for the full re-decision
+  h.full_count_bytes = align_up(static_cast<size_t>(s.n_rounds) * sizeof(int32_t), 256);
+  h.full_list_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_tokens * sizeof(int32_t), 256);
+  h.total = h.frag_bytes + h.rt_bytes + h.bound_bytes + h.counter_bytes + h.list_bytes + h.full_count_bytes +
+            h.full_list_bytes;
   return h;
 }
 
@@ -1010,6 +1139,10 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += h.counter_bytes;
   int32_t* list = reinterpret_cast<int32_t*>(ws);
+  ws += h.list_bytes;
+  int32_t* full_count = reinterpret_cast<int32_t*>(ws);
+  ws += h.full_count_bytes;
+  int32_t* full_list = reinterpret_cast<int32_t*>(ws);
   const int n_regions = (s.n_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
   const int cap = kTokensPerBlock * s.n_rounds;
   NearTieList lst{counts, list, cap, nullptr};
@@ -1019,22 +1152,28 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<64>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      if (s.n_ctiles >= kSignAtEndTiles)
+        hipLaunchKernelGGL((hash_mfma_kernel<64, true>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      else
+        hipLaunchKernelGGL((hash_mfma_kernel<64, false>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_mfma_kernel<128>, grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      if (s.n_ctiles >= kSignAtEndTiles)
+        hipLaunchKernelGGL((hash_mfma_kernel<128, true>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      else
+        hipLaunchKernelGGL((hash_mfma_kernel<128, false>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
     }
   } else {
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     }
@@ -1043,14 +1182,28 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   const int fix_blocks = std::min(n_regions, 2048);
   if (s.d == 64) {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
+  }
+  // full re-decisions: batches of each round's list (the grid covers up to
+  // kFullBatch * 64 entries per round at once and loops over the rest)
+  const dim3 full_grid(64, s.n_rounds);
+  if (s.d == 64) {
+    if (bf16)
+      hipLaunchKernelGGL((hash_full_kernel<64, true>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
+    else
+      hipLaunchKernelGGL((hash_full_kernel<64, false>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((hash_full_kernel<128, true>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
+    else
+      hipLaunchKernelGGL((hash_full_kernel<128, false>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
   }
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();
