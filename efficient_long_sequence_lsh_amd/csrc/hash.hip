@@ -21,7 +21,7 @@
 //     the sign cleared and a candidate code in the low mantissa bits.  A
 //     running top-two of keys per lane takes a med3, a max and a max3 per two
 //     values; once per tile the lane's top two are merged into a running top
-//     three.  The sign is left out of the keys: with many column tiles per
+//     four.  The sign is left out of the keys: with many column tiles per
 //     round, the leader's projection is recomputed at the end of the round
 //     from x . R_hi alone (v_dot2 on the bf16 operands the lane already
 //     holds), whose error bound shows its sign is that of the exact
@@ -31,11 +31,12 @@
 //   * The leading keys give the two leading candidates and their gap.  When the
 //     gap is below twice a bound on the error of one projection (plus the key
 //     truncation), the (position, round) is queued and a fix-up kernel
-//     re-decides it in float64: between those two candidates when the third
-//     key is provably more than the bound below the leader, otherwise over all
-//     columns (keys rank candidates that share a truncation bin by code, not
-//     by value, so only a bound on everything outside the top two makes the
-//     pair re-decision exact).  By Cauchy-Schwarz, with x6
+//     re-decides it in float64 over the smallest set of columns that the four
+//     keys prove holds the winner: the top two, the top three, one lane's 16
+//     columns of a tile with or without one more, or all columns (keys rank
+//     candidates that share a truncation bin by code, not by value, so the
+//     set must cover every candidate not bounded below the leader; see
+//     decide_and_store).  By Cauchy-Schwarz, with x6
 //     and R_lo6 the fp6 operands, one projection is off by at most
 //       |x| max_j |R_j - R_hi,j - R_lo6,j| + |x - x6| max_j |R_lo6,j|
 //     plus float32 accumulation (below 2^-15 (|x| max_j |R_j| + |x6| max_j
@@ -87,31 +88,41 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
 }
 
-// Exact top-three of single keys (float32 path): k1 >= k2 >= k3.
-__device__ __forceinline__ void top3_push(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t key) {
-  k3 = umed3(k2, k3, key);
-  k2 = umed3(k1, k2, key);
-  k1 = max(k1, key);
+// The four largest keys, k1 >= k2 >= k3 >= k4.  The n-th largest of two
+// sorted lists A, B is the largest min(A_i, B_j) over i + j = n (A_0 = B_0 =
+// +inf), which max3/min/med3 networks evaluate.
+struct Top4 {
+  uint32_t k1, k2, k3, k4;
+};
+
+// One key into the four (float32 path: every projection on its own).
+__device__ __forceinline__ void top4_push(Top4& t, uint32_t key) {
+  t.k4 = umed3(t.k3, t.k4, key);
+  t.k3 = umed3(t.k2, t.k3, key);
+  t.k2 = umed3(t.k1, t.k2, key);
+  t.k1 = max(t.k1, key);
 }
 
-// The three largest of {k1 >= k2 >= k3} and a sorted pair {a >= b}: the n-th
-// largest of two sorted lists is the largest min(A_i, B_j) over i + j = n.
-__device__ __forceinline__ void top3_merge2(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t a, uint32_t b) {
-  const uint32_t n3 = max(max(k3, min(k2, a)), min(k1, b));
-  const uint32_t n2 = max(min(k1, a), max(k2, b));
-  k1 = max(k1, a);
-  k2 = n2;
-  k3 = n3;
+// A sorted pair {a >= b} into the four.
+__device__ __forceinline__ void top4_merge2(Top4& t, uint32_t a, uint32_t b) {
+  const uint32_t n4 = max(max(t.k4, min(t.k3, a)), min(t.k2, b));
+  const uint32_t n3 = max(max(t.k3, min(t.k2, a)), min(t.k1, b));
+  const uint32_t n2 = max(max(t.k2, min(t.k1, a)), b);
+  t.k1 = max(t.k1, a);
+  t.k2 = n2;
+  t.k3 = n3;
+  t.k4 = n4;
 }
 
-// The three largest of two sorted triples.
-__device__ __forceinline__ void top3_merge3(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t a1, uint32_t a2,
-                                            uint32_t a3) {
-  const uint32_t n3 = max(max(max(k3, a3), min(k2, a1)), min(k1, a2));
-  const uint32_t n2 = max(min(k1, a1), max(k2, a2));
-  k1 = max(k1, a1);
-  k2 = n2;
-  k3 = n3;
+// Two sorted fours.
+__device__ __forceinline__ void top4_merge4(Top4& t, const Top4& o) {
+  const uint32_t n4 = max(max(max(t.k4, o.k4), max(min(t.k3, o.k1), min(t.k1, o.k3))), min(t.k2, o.k2));
+  const uint32_t n3 = max(max(t.k3, o.k3), max(min(t.k2, o.k1), min(t.k1, o.k2)));
+  const uint32_t n2 = max(max(t.k2, o.k2), min(t.k1, o.k1));
+  t.k1 = max(t.k1, o.k1);
+  t.k2 = n2;
+  t.k3 = n3;
+  t.k4 = n4;
 }
 
 __device__ __forceinline__ float key_magnitude(uint32_t key, uint32_t code_mask) {
@@ -124,66 +135,104 @@ constexpr int kTokensPerBlock = 256;
 
 struct NearTieList {
   int32_t* counts;    // per workgroup: number of queued entries
-  int32_t* entries;   // 3 per entry: token, round | kind<<30, c1 | c2<<16
+  int32_t* entries;   // 3 per entry: token; round | kind<<16 | c<<18; a | b<<16
   int cap;            // entries per workgroup region
   int* lds_count;     // the workgroup's counter in LDS (set inside the kernel)
 };
 
-// What a queued (position, round) is re-decided over.
+// What a queued (position, round) is re-decided over (columns a, b, c as
+// packed in its entry; rounds < 2^16 and columns < 2^13 by the entry points'
+// limits).
 enum NearTieKind : int {
-  kTiePair = 0,    // the two leading candidates c1, c2
-  kTieGroup = 1,   // the 16 columns of c1's group (one lane's projections of one tile)
-  kTieFull = 2,    // every column
+  kTiePair = 0,     // columns a, b
+  kTieTriple = 1,   // columns a, b, c
+  kTieGroup = 2,    // the 16 columns of a's group (one lane's projections of one tile), plus column b unless 0xffff
+  kTieFull = 3,     // every column
 };
+constexpr int kNoColumn = 0xffff;
 
-__device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int round, int kind, int c1, int c2) {
+__device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int round, int kind, int a, int b, int c) {
   int idx = atomicAdd(lst.lds_count, 1);
   int32_t* e = lst.entries + 3 * (static_cast<size_t>(blockIdx.x) * lst.cap + idx);
   e[0] = tok;
-  e[1] = round | (kind << 30);
-  e[2] = (c1 & 0xffff) | (c2 << 16);
+  e[1] = round | (kind << 16) | (c << 18);
+  e[2] = (a & 0xffff) | (b << 16);
 }
 
-// Shared decision once a token's three leading keys and |x|_2 are known.
+// Shared decision once a token's four leading keys and |x|_2 are known.
 // tau_x bounds the error of the gap between two projections before key
 // truncation, which is added here.  Keys order candidates by truncated
 // magnitude and, inside one truncation bin, by candidate code, so a candidate
-// can rank below others whose projections are smaller.
+// can rank below others whose projections are smaller; the fix-up must
+// therefore re-score every candidate that cannot be bounded more than tau
+// below the leader.
 //
-// k3 is the third of the union of every group's top two keys (a group is one
-// lane's 16 projections of one tile in the MFMA kernel, a single projection
-// in the float32 kernel).  When k1 and k2 come from different groups, k3 is
-// the overall third key, so every candidate outside the top two has a
-// truncated magnitude at most m3.  When they come from one group G, every
-// candidate outside G is at most m3 (its group's best key is in the union
-// below k1, k2), but G's own third is unknown.  So:
-//   m1 - m2 > tau                  -> the leader wins outright;
-//   else m1 - m3 > tau, two groups -> float64 re-decision between the top two;
-//   else m1 - m3 > tau, one group  -> float64 re-decision over G's columns;
-//   else                           -> float64 re-decision over all columns
-// (also when even the leader's magnitude is within tau, e.g. x = 0, or when
-// the caller cannot vouch for the sign of the leader's projection: sign_ok).
+// The four keys are the top four of U, the union of every group's top two
+// (GROUPS: a group is one lane's 16 projections of one tile, code >> 4;
+// otherwise every projection is its own group and the keys are exact).  A
+// projection outside U has two larger ones in its own group.  With g(k) the
+// group of key k and m1..m4 the truncated magnitudes:
+//   m1 - m2 > tau: the leader wins outright (the overall second is in U);
+//   g(k1) != g(k2): the overall third is k3, so
+//     m1 - m3 > tau                     -> re-decide {c1, c2};
+//     else, g(k3) a third group         -> the overall fourth is k4:
+//       m1 - m4 > tau                   -> re-decide {c1, c2, c3};
+//     else, k3 shares a group G with k1 or k2: every projection outside G
+//       and the other leader is at most m4 (the other leader's group has
+//       its second in U below k3, every other group its best):
+//       m1 - m4 > tau                   -> re-decide G + the other leader;
+//   g(k1) == g(k2) = G: every projection outside G is at most m3:
+//     m1 - m3 > tau                     -> re-decide G;
+//     m1 - m4 > tau                     -> re-decide G + c3 (k3's group has
+//                                          its second in U below k3);
+//   anything else, or m1 itself within tau (e.g. x = 0), or the caller
+//   cannot vouch for the sign of the leader's projection (sign_ok)
+//                                       -> re-decide every column.
 // positive is the sign of the leader's projection, which picks bucket c1 or
-// c1 + b/2.
-__device__ __forceinline__ void decide_and_store(uint32_t k1, uint32_t k2, uint32_t k3, bool same_group, bool positive,
-                                                 bool sign_ok, int col1, int col2, float tau_x, int code_bits, int half,
-                                                 int tok, int seq_len, int n_rounds, int round, int32_t* buckets,
+// c1 + b/2; the float64 re-decisions take their own signs.
+template <bool GROUPS>
+__device__ __forceinline__ void decide_and_store(const Top4& t, bool positive, bool sign_ok, int col1, int col2,
+                                                 int col3, float tau_x, int code_bits, int half, int tok,
+                                                 int seq_len, int n_rounds, int round, int32_t* buckets,
                                                  NearTieList lst) {
   const uint32_t code_mask = (1u << code_bits) - 1u;
-  const float m1 = key_magnitude(k1, code_mask);
-  const float m2 = key_magnitude(k2, code_mask);
-  const float m3 = key_magnitude(k3, code_mask);
+  const float m1 = key_magnitude(t.k1, code_mask);
+  const float m2 = key_magnitude(t.k2, code_mask);
+  const float m3 = key_magnitude(t.k3, code_mask);
+  const float m4 = key_magnitude(t.k4, code_mask);
   const float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
   const int bucket = col1 + (positive ? 0 : half);
   const int bh = tok / seq_len, pos = tok - bh * seq_len;
   buckets[(static_cast<size_t>(bh) * n_rounds + round) * seq_len + pos] = bucket;
   const bool tiny = !(m1 > tau) || !sign_ok;
   const bool near = !((m1 - m2) > tau);
-  const bool third_far = (m1 - m3) > tau;
-  if (tiny || near) {
-    const int kind = (tiny || !third_far) ? kTieFull : same_group ? kTieGroup : kTiePair;
-    push_near_tie(lst, tok, round, kind, col1, col2);
+  if (!tiny && !near) return;
+  int kind = kTieFull, a = col1, b = col2, c = 0;
+  if (!tiny) {
+    constexpr int kShift = GROUPS ? 4 : 0;
+    const uint32_t g1 = (t.k1 & code_mask) >> kShift, g2 = (t.k2 & code_mask) >> kShift;
+    const uint32_t g3 = (t.k3 & code_mask) >> kShift;
+    const bool far3 = (m1 - m3) > tau, far4 = (m1 - m4) > tau;
+    if (g1 != g2) {
+      if (far3) {
+        kind = kTiePair;
+      } else if (far4) {
+        if (g3 != g1 && g3 != g2) {
+          kind = kTieTriple;
+          c = col3;
+        } else {
+          kind = kTieGroup;   // k3's group and the leader outside it
+          a = col3;
+          b = g3 == g1 ? col2 : col1;
+        }
+      }
+    } else if (far3 || far4) {
+      kind = kTieGroup;
+      a = col1;
+      b = far3 ? kNoColumn : col3;
+    }
   }
+  push_near_tie(lst, tok, round, kind, a, b, c);
 }
 
 // The float32 bounds assume that the products and partial sums that matter
@@ -302,7 +351,7 @@ template <int D, bool FRAG>
 __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restrict__ rot, int half, int n_rounds,
                                                            int n_ctiles, u32x4* __restrict__ frag,
                                                            float* __restrict__ rt, uint32_t* __restrict__ bound_bits,
-                                                           int32_t* n_near_ties, int32_t* __restrict__ full_count) {
+                                                           int32_t* n_near_ties) {
   using FT = FragTile<D>;
   constexpr int kGroups = 8;               // k-ranges per column
   constexpr int kPerG = D / kGroups;       // 8 or 16 values
@@ -405,8 +454,6 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
     max32_to(c < half ? norm_bits_up(sum) : 0u, bound_bits + kBoundCmax * term + slot);
     // the caller's near-tie total starts from zero (the fix-up kernel adds to it)
     if (threadIdx.x == 0 && t == 0 && r == 0 && n_near_ties != nullptr) *n_near_ties = 0;
-    // this round's list of full re-decisions starts empty (the fix-up kernel appends)
-    if (threadIdx.x == 0 && t == 0) full_count[r] = 0;
     if (FRAG) {
       double sr = 0.0, sl = 0.0;
 #pragma unroll
@@ -528,8 +575,10 @@ __device__ __forceinline__ i32x8 x_to_fp6(const uint16_t* __restrict__ xrow, boo
 // gap would be zero and the fix-up would decide).
 constexpr int kSignAtEndTiles = 32;   // column tiles per round from which SIGN_AT_END is used
 
+// Three wavefronts per SIMD at d = 64 fit only without the running maximum's
+// registers; the running-maximum variant takes two (no spills in the loop).
 template <int D, bool SIGN_AT_END>
-__global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kernel(
+__global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) void hash_mfma_kernel(
     const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ bound_bits,
     HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
   using FT = FragTile<D>;
@@ -613,13 +662,12 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
 
   const uint32_t code_mask = (1u << s.code_bits) - 1u;
   const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
-  // Running top three of the per-lane, per-tile top twos (a "group" is one
-  // lane's 16 projections of one tile): the overall third-largest key is k3
-  // unless k1 and k2 come from the same group (see round_end).
-  uint32_t k1[kStrips], k2[kStrips], k3[kStrips];
+  // Running top four of the per-lane, per-tile top twos (a "group" is one
+  // lane's 16 projections of one tile; decide_and_store says what they bound).
+  Top4 tk[kStrips];
   int32_t smax[kStrips];
 #pragma unroll
-  for (int st = 0; st < kStrips; ++st) { k1[st] = 0u; k2[st] = 0u; k3[st] = 0u; smax[st] = INT32_MIN; }
+  for (int st = 0; st < kStrips; ++st) { tk[st] = Top4{0u, 0u, 0u, 0u}; smax[st] = INT32_MIN; }
 
   // Projections of tile n (lds buffer n & 1) into acc.
   auto mfma_tile = [&](f32x16 (&acc)[kStrips], const u32x4* cur) {
@@ -669,7 +717,7 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
         for (int i = 0; i < 16; i += 2) sm = max(max(sm, __float_as_int(acc[st][i])), __float_as_int(acc[st][i + 1]));
         smax[st] = sm;
       }
-      top3_merge2(k1[st], k2[st], k3[st], t1 | tile_code, t2 | tile_code);
+      top4_merge2(tk[st], t1 | tile_code, t2 | tile_code);
     }
   };
   // After the last tile of a round: merge the two lanes that share each
@@ -692,9 +740,10 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
     };
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
-      const uint32_t o1 = shfl_xor_u(k1[st], 32), o2 = shfl_xor_u(k2[st], 32), o3 = shfl_xor_u(k3[st], 32);
-      top3_merge3(k1[st], k2[st], k3[st], o1, o2, o3);   // the same on both lanes of the token
-      const uint32_t c1 = k1[st] & code_mask, c2 = k2[st] & code_mask;
+      const Top4 other{shfl_xor_u(tk[st].k1, 32), shfl_xor_u(tk[st].k2, 32), shfl_xor_u(tk[st].k3, 32),
+                       shfl_xor_u(tk[st].k4, 32)};
+      top4_merge4(tk[st], other);   // the same on both lanes of the token (the merge is symmetric)
+      const uint32_t c1 = tk[st].k1 & code_mask, c2 = tk[st].k2 & code_mask, c3 = tk[st].k3 & code_mask;
       const int col1 = col_of(c1);
       float sd = 0.0f;
       if (SIGN_AT_END) {
@@ -731,19 +780,14 @@ __global__ __launch_bounds__(kHashThreads, D == 128 ? 2 : 3) void hash_mfma_kern
           // tau_x plus that error.
           const float e_sign = (xn.x * (rho1 + rho2) + kAccRel * xn.x * cmax) * (1.0f + 1.0f / 1024.0f);
           positive = sd > 0.0f;
-          sign_ok = key_magnitude(k1[st], code_mask) > tau_x + e_sign;
+          sign_ok = key_magnitude(tk[st].k1, code_mask) > tau_x + e_sign;
         } else {
-          positive = sm >= static_cast<int32_t>(k1[st] & ~code_mask);
+          positive = sm >= static_cast<int32_t>(tk[st].k1 & ~code_mask);
         }
-        // a group is one lane's 16 projections of one tile: code >> 4 is
-        // (tile, lane half)
-        const bool same_group = ((c1 ^ c2) >> 4) == 0u;
-        decide_and_store(k1[st], k2[st], k3[st], same_group, positive, sign_ok, col1, col_of(c2), tau_x, s.code_bits,
-                         s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
+        decide_and_store<true>(tk[st], positive, sign_ok, col1, col_of(c2), col_of(c3), tau_x, s.code_bits, s.half,
+                               tok, s.seq_len, s.n_rounds, round, buckets, lst);
       }
-      k1[st] = 0u;
-      k2[st] = 0u;
-      k3[st] = 0u;
+      tk[st] = Top4{0u, 0u, 0u, 0u};
       smax[st] = INT32_MIN;
     }
   };
@@ -830,7 +874,7 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
   const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
   for (int round = 0; round < s.n_rounds; ++round) {
     const float* R = rot + static_cast<size_t>(round) * D * s.half;
-    uint32_t k1 = 0u, k2 = 0u, k3 = 0u;
+    Top4 tk{0u, 0u, 0u, 0u};
     int32_t smax = INT32_MIN;
     for (int c0 = 0; c0 < s.half; c0 += kCols) {
       __syncthreads();
@@ -843,21 +887,22 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
         float p = 0.0f;
 #pragma unroll
         for (int k = 0; k < D; ++k) p = fmaf(x[k], rt[k][j], p);
-        top3_push(k1, k2, k3, make_key(p, keep_mask, static_cast<uint32_t>(c0 + j)));
+        top4_push(tk, make_key(p, keep_mask, static_cast<uint32_t>(c0 + j)));
         smax = max(smax, __float_as_int(p));
       }
     }
     const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
     if (live) {
-      int c1 = static_cast<int>(k1 & code_mask), c2 = static_cast<int>(k2 & code_mask);
+      const int c1 = static_cast<int>(tk.k1 & code_mask), c2 = static_cast<int>(tk.k2 & code_mask);
+      const int c3 = static_cast<int>(tk.k3 & code_mask);
       // the leader is positive exactly when the largest raw bit pattern as a
       // signed integer (the largest positive projection, if any) reaches its
       // truncated magnitude; were it negative while a positive projection
       // reached that magnitude, the two would share a truncated magnitude, so
       // the gap would be zero and the fix-up would decide
-      const bool positive = smax >= static_cast<int32_t>(k1 & ~code_mask);
-      decide_and_store(k1, k2, k3, false, positive, true, c1, c2, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
-                       s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
+      const bool positive = smax >= static_cast<int32_t>(tk.k1 & ~code_mask);
+      decide_and_store<false>(tk, positive, true, c1, c2, c3, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
+                              s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
   __syncthreads();
@@ -868,23 +913,29 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
 // Re-decide queued (token, round) pairs in float64: products of a bf16 or
 // float32 feature and a float32 rotation entry are exact in float64, and a
 // D-term sum rounds by at most about D * 2^-53 of |x| max_j |R_j|.
-//  * pair and group entries take one group of 16 lanes each.  Pair: lane i
-//    holds features [i*D/16, (i+1)*D/16) and the two column dot products are
-//    summed across the 16 lanes.  Group: lane i scores column i of the group
-//    (a whole dot product, the column read from the transposed copy).
-//  * full entries are appended to their round's list for hash_full_kernel.
+//  * pair, triple and group entries take one group of 16 lanes each.  A
+//    listed column's dot product is split over the lanes by features (lane i
+//    holds features [i*D/16, (i+1)*D/16)) and summed across them; a group's
+//    16 columns go one per lane (a whole dot product each).  Columns are read
+//    from the transposed float32 copy of R (one contiguous row per column).
+//  * full entries (rare: four candidates within the bound) take the whole
+//    workgroup: x staged in LDS as float64, thread t scores columns t,
+//    t + 256, ... from R's original [k][column] layout (a wavefront reads
+//    64 consecutive floats per feature), 32 loads in flight per column.
 // Best candidate as (value, bucket): the larger value wins, equal values go
 // to the lower bucket; p == 0 counts as +p (the lower bucket).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
-                                                         HashShape s,
+                                                         const float* __restrict__ rot, HashShape s,
                                                          int32_t* __restrict__ buckets,
                                                          const int32_t* __restrict__ counts, int n_regions, int cap,
-                                                         const int32_t* __restrict__ entries_all, int32_t* n_near_ties,
-                                                         int32_t* __restrict__ full_count,
-                                                         int32_t* __restrict__ full_list) {
+                                                         const int32_t* __restrict__ entries_all, int32_t* n_near_ties) {
   constexpr int kPer = D / 16;
   constexpr int kGroups = 256 / 16;
+  constexpr int kWaves = 256 / 64;
+  __shared__ double xs[D];
+  __shared__ double red_v[kWaves];
+  __shared__ int red_b[kWaves];
   const int sub = threadIdx.x & 15;
   const int group = threadIdx.x >> 4;
   auto xval = [&](int tok, int k) -> double {
@@ -916,161 +967,97 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
       const int tok = entries[3 * static_cast<size_t>(e)];
       const int w1 = entries[3 * static_cast<size_t>(e) + 1];
       const int w2 = entries[3 * static_cast<size_t>(e) + 2];
-      const int round = w1 & 0x3fffffff;
-      const int kind = (w1 >> 30) & 3;
-      if (kind == kTieFull) {   // the same for all 16 lanes of the group
-        if (sub == 0) full_list[static_cast<size_t>(round) * s.n_tokens + atomicAdd(&full_count[round], 1)] = tok;
-        continue;
-      }
+      const int round = w1 & 0xffff;
+      const int kind = (w1 >> 16) & 3;
+      if (kind == kTieFull) continue;   // the same for all 16 lanes of the group
       const float* Rt = rt + static_cast<size_t>(round) * s.half * D;
+      const int a = w2 & 0xffff, b = (w2 >> 16) & 0xffff, c = (w1 >> 18) & 0x1fff;
       double best_v = -1.0;
       int best_b = 0x7fffffff;
-      const int c1 = w2 & 0xffff;
-      if (kind == kTiePair) {
-        const int c2 = (w2 >> 16) & 0xffff;
-        double xv[kPer];
+      // listed columns scored cooperatively (features split over the lanes)
+      int cols[3] = {kNoColumn, kNoColumn, kNoColumn};
+      if (kind == kTiePair || kind == kTieTriple) {
+        cols[0] = a;
+        cols[1] = b;
+        if (kind == kTieTriple) cols[2] = c;
+      } else {
+        cols[0] = b;   // the group's extra column, if any
+      }
+      double xv[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) xv[i] = xval(tok, sub * kPer + i);
-        double p1 = 0.0, p2 = 0.0;
-        const f32x4* r1 = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(min(c1, s.half - 1)) * D + sub * kPer);
-        const f32x4* r2 = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(min(c2, s.half - 1)) * D + sub * kPer);
+      for (int i = 0; i < kPer; ++i) xv[i] = xval(tok, sub * kPer + i);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (cols[j] >= s.half) continue;   // absent or a padding column: the same for the 16 lanes
+        const f32x4* r = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(cols[j]) * D + sub * kPer);
+        double p = 0.0;
 #pragma unroll
         for (int i = 0; i < kPer / 4; ++i) {
-          const f32x4 a = r1[i], b = r2[i];
+          const f32x4 v = r[i];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p1 += xv[4 * i + j] * static_cast<double>(a[j]);
-            p2 += xv[4 * i + j] * static_cast<double>(b[j]);
-          }
+          for (int q = 0; q < 4; ++q) p += xv[4 * i + q] * static_cast<double>(v[q]);
         }
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-          p1 += shfl_xor_d(p1, off);
-          p2 += shfl_xor_d(p2, off);
-        }
-        if (c1 < s.half) offer(best_v, best_b, p1, c1);
-        if (c2 < s.half && c2 != c1) offer(best_v, best_b, p2, c2);
-      } else {
-        // c1's group: tile c1 / 32, lane half (c1 / 4) % 2; lane i takes its
+        for (int off = 8; off > 0; off >>= 1) p += shfl_xor_d(p, off);
+        offer(best_v, best_b, p, cols[j]);
+      }
+      if (kind == kTieGroup) {
+        // a's group: tile a / 32, lane half (a / 4) % 2; lane i takes its
         // projection i, column 32 t + 8 (i / 4) + 4 half + i % 4
-        const int c = 32 * (c1 >> 5) + 8 * (sub >> 2) + 4 * ((c1 >> 2) & 1) + (sub & 3);
-        if (c < s.half) {
-          const f32x4* rc = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(c) * D);
+        const int col = 32 * (a >> 5) + 8 * (sub >> 2) + 4 * ((a >> 2) & 1) + (sub & 3);
+        if (col < s.half) {
+          const f32x4* rc = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(col) * D);
           double p = 0.0;
 #pragma unroll 4
           for (int i = 0; i < D / 4; ++i) {
-            const f32x4 a = rc[i];
+            const f32x4 v = rc[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p += xval(tok, 4 * i + j) * static_cast<double>(a[j]);
+            for (int q = 0; q < 4; ++q) p += xval(tok, 4 * i + q) * static_cast<double>(v[q]);
           }
-          offer(best_v, best_b, p, c);
+          offer(best_v, best_b, p, col);
         }
         merge_lanes(best_v, best_b, 8);
       }
       if (sub == 0) store(tok, round, best_b);
     }
-  }
-  if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
-}
-
-// Full re-decisions, batched: a workgroup takes kFullBatch positions of one
-// round's list and stages their features in LDS as float64.  Rotation columns
-// go through LDS in tiles of 64 (all of a tile's loads in flight, the next
-// tile loaded into registers while the current one is scored; R's original
-// [k][column] layout, so every wavefront load reads 256 contiguous bytes).
-// Wavefront w scores positions 2w and 2w + 1 against the tile's 64 columns,
-// one column per lane, and keeps each position's best over the columns it
-// has seen; a wavefront reduction gives the bucket.
-constexpr int kFullBatch = 8;
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void hash_full_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rot,
-                                                        HashShape s, int32_t* __restrict__ buckets,
-                                                        const int32_t* __restrict__ full_count,
-                                                        const int32_t* __restrict__ full_list) {
-  constexpr int E = kFullBatch;
-  constexpr int kCols = 64;
-  constexpr int kPer = D * kCols / 256;   // tile entries loaded per thread
-  static_assert(E == 2 * (256 / 64), "two positions per wavefront");
-  __shared__ double xs[D][E];
-  __shared__ float tile[2][D][kCols];
-  __shared__ int toks[E];
-  const int round = blockIdx.y;
-  const int count = full_count[round];
-  const int32_t* list = full_list + static_cast<size_t>(round) * s.n_tokens;
-  const float* R = rot + static_cast<size_t>(round) * D * s.half;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_tiles = (s.half + kCols - 1) / kCols;
-  // tile entry i of this thread: feature (threadIdx.x + 256 i) / 64, column (threadIdx.x + 256 i) % 64 = lane
-  auto load_tile = [&](float (&v)[kPer], int t) {
-    const int c = t * kCols + lane;
+    // Full entries, one at a time for the whole workgroup (the entry list and
+    // the loop bounds are the same for every thread).
+    for (int e = 0; e < count; ++e) {
+      const int w1 = entries[3 * static_cast<size_t>(e) + 1];
+      if (((w1 >> 16) & 3) != kTieFull) continue;
+      const int tok = entries[3 * static_cast<size_t>(e)];
+      const int round = w1 & 0xffff;
+      __syncthreads();   // earlier readers of xs, red_v and red_b are done
+      if (threadIdx.x < D) xs[threadIdx.x] = xval(tok, threadIdx.x);
+      __syncthreads();
+      const float* R = rot + static_cast<size_t>(round) * D * s.half;
+      double best_v = -1.0;
+      int best_b = 0x7fffffff;
+      for (int c = threadIdx.x; c < s.half; c += 256) {
+        double p = 0.0;
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          float rv[32];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int k = (threadIdx.x >> 6) + 4 * i;
-      v[i] = c < s.half ? R[static_cast<size_t>(k) * s.half + c] : 0.0f;
-    }
-  };
-  for (int base = blockIdx.x * E; base < count; base += gridDim.x * E) {
-    const int ne = min(E, count - base);
-    __syncthreads();   // earlier readers of toks, xs and tile are done
-    if (threadIdx.x < E) toks[threadIdx.x] = threadIdx.x < ne ? list[base + threadIdx.x] : -1;
-    __syncthreads();
-    for (int u = threadIdx.x; u < E * D; u += 256) {
-      const int e = u / D, k = u - e * D;
-      const int tok = toks[e];
-      double xv = 0.0;
-      if (tok >= 0) {
-        const size_t at = static_cast<size_t>(tok) * D + k;
-        xv = BF16 ? static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[at]))
-                  : static_cast<double>(static_cast<const float*>(qk_raw)[at]);
-      }
-      xs[k][e] = xv;
-    }
-    float v[kPer];
-    load_tile(v, 0);
-    double bv0 = -1.0, bv1 = -1.0;
-    int bb0 = 0x7fffffff, bb1 = 0x7fffffff;
-    const int e0 = 2 * wave, e1 = 2 * wave + 1;
-    for (int t = 0; t < n_tiles; ++t) {
-      float (&cur)[D][kCols] = tile[t & 1];
+          for (int k = 0; k < 32; ++k) rv[k] = R[static_cast<size_t>(k0 + k) * s.half + c];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) cur[(threadIdx.x >> 6) + 4 * i][lane] = v[i];
-      __syncthreads();   // the tile (and, first time round, xs) is in LDS
-      if (t + 1 < n_tiles) load_tile(v, t + 1);
-      double p0 = 0.0, p1 = 0.0;
-#pragma unroll 8
-      for (int k = 0; k < D; ++k) {
-        const double r = static_cast<double>(cur[k][lane]);
-        p0 += xs[k][e0] * r;
-        p1 += xs[k][e1] * r;
+          for (int k = 0; k < 32; ++k) p += xs[k0 + k] * static_cast<double>(rv[k]);
+        }
+        offer(best_v, best_b, p, c);
       }
-      const int c = t * kCols + lane;
-      if (c < s.half) {
-        const double a0 = p0 >= 0.0 ? p0 : -p0, a1 = p1 >= 0.0 ? p1 : -p1;
-        const int b0 = p0 >= 0.0 ? c : c + s.half, b1 = p1 >= 0.0 ? c : c + s.half;
-        if (a0 > bv0 || (a0 == bv0 && b0 < bb0)) { bv0 = a0; bb0 = b0; }
-        if (a1 > bv1 || (a1 == bv1 && b1 < bb1)) { bv1 = a1; bb1 = b1; }
+      merge_lanes(best_v, best_b, 32);
+      if ((threadIdx.x & 63) == 0) {
+        red_v[threadIdx.x >> 6] = best_v;
+        red_b[threadIdx.x >> 6] = best_b;
       }
-      // the other buffer is rewritten next step only after this barrier
-      // has been passed by every wavefront, which the next step's barrier
-      // orders (two buffers)
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-      const double o0 = shfl_xor_d(bv0, off), o1 = shfl_xor_d(bv1, off);
-      const int c0 = __shfl_xor(bb0, off, 64), c1 = __shfl_xor(bb1, off, 64);
-      if (o0 > bv0 || (o0 == bv0 && c0 < bb0)) { bv0 = o0; bb0 = c0; }
-      if (o1 > bv1 || (o1 == bv1 && c1 < bb1)) { bv1 = o1; bb1 = c1; }
-    }
-    if (lane == 0) {
-      for (int j = 0; j < 2; ++j) {
-        const int e = 2 * wave + j;
-        if (e >= ne) continue;
-        const int tok = toks[e];
-        const int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
-        buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = j == 0 ? bb0 : bb1;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int w = 1; w < kWaves; ++w)
+          if (red_v[w] > best_v || (red_v[w] == best_v && red_b[w] < best_b)) { best_v = red_v[w]; best_b = red_b[w]; }
+        store(tok, round, best_b);
       }
     }
   }
+  if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
 }
 
 __global__ void fill_zero_kernel(int32_t* p, size_t n) {
@@ -1111,11 +1098,7 @@ HashScratch hash_scratch(const HashShape& s) {
   const size_t regions = (static_cast<size_t>(s.n_tokens) + kTokensPerBlock - 1) / kTokensPerBlock;
   h.counter_bytes = align_up(regions * sizeof(int32_t), 256);
   h.list_bytes = align_up(regions * kTokensPerBlock * s.n_rounds * 3 * sizeof(int32_t), 256);
-  // per round: a counter and up to n_tokens positions for the full re-decision
-  h.full_count_bytes = align_up(static_cast<size_t>(s.n_rounds) * sizeof(int32_t), 256);
-  h.full_list_bytes = align_up(static_cast<size_t>(s.n_rounds) * s.n_tokens * sizeof(int32_t), 256);
-  h.total = h.frag_bytes + h.rt_bytes + h.bound_bytes + h.counter_bytes + h.list_bytes + h.full_count_bytes +
-            h.full_list_bytes;
+  h.total = h.frag_bytes + h.rt_bytes + h.bound_bytes + h.counter_bytes + h.list_bytes;
   return h;
 }
 
@@ -1139,10 +1122,7 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   ws += h.counter_bytes;
   int32_t* list = reinterpret_cast<int32_t*>(ws);
-  ws += h.list_bytes;
-  int32_t* full_count = reinterpret_cast<int32_t*>(ws);
-  ws += h.full_count_bytes;
-  int32_t* full_list = reinterpret_cast<int32_t*>(ws);
+
   const int n_regions = (s.n_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
   const int cap = kTokensPerBlock * s.n_rounds;
   NearTieList lst{counts, list, cap, nullptr};
@@ -1152,14 +1132,14 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       if (s.n_ctiles >= kSignAtEndTiles)
         hipLaunchKernelGGL((hash_mfma_kernel<64, true>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
       else
         hipLaunchKernelGGL((hash_mfma_kernel<64, false>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       if (s.n_ctiles >= kSignAtEndTiles)
         hipLaunchKernelGGL((hash_mfma_kernel<128, true>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
@@ -1169,11 +1149,11 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   } else {
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
-      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
+      hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     } else {
-      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties, full_count);
+      hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
     }
@@ -1182,28 +1162,14 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
   const int fix_blocks = std::min(n_regions, 2048);
   if (s.d == 64) {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
+      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
     else
-      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, s, buckets, counts, n_regions, cap, list, n_near_ties, full_count, full_list);
-  }
-  // full re-decisions: batches of each round's list (the grid covers up to
-  // kFullBatch * 64 entries per round at once and loops over the rest)
-  const dim3 full_grid(64, s.n_rounds);
-  if (s.d == 64) {
-    if (bf16)
-      hipLaunchKernelGGL((hash_full_kernel<64, true>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
-    else
-      hipLaunchKernelGGL((hash_full_kernel<64, false>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL((hash_full_kernel<128, true>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
-    else
-      hipLaunchKernelGGL((hash_full_kernel<128, false>), full_grid, dim3(256), 0, stream, qk, rotations, s, buckets, full_count, full_list);
+      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
   }
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();

@@ -28,8 +28,6 @@ struct HashScratch {
   size_t bound_bytes;    // per-tile column-norm maxima of the error-bound terms (float bits)
   size_t counter_bytes;  // near-tie counter
   size_t list_bytes;     // near-tie list (3 int32 per entry, capacity n_tokens * n_rounds)
-  size_t full_count_bytes;  // per round: number of positions queued for a full re-decision
-  size_t full_list_bytes;   // per round: those positions (capacity n_tokens each)
   size_t total;
 };
 HashScratch hash_scratch(const HashShape& s);
