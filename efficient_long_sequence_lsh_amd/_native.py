@@ -32,6 +32,7 @@ SIGNATURES = {
     "reformer_lsh_version": (_i, []),
     "reformer_lsh_hash_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "reformer_lsh_hash": (_i, [_p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]),
+    "reformer_lsh_hash_noalloc": (_i, [_p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "reformer_lsh_sort_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "reformer_lsh_sort": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]),
     "reformer_lsh_chunk_attend": (_i, [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
@@ -131,6 +132,32 @@ def lsh_hash(qk: torch.Tensor, rotations: torch.Tensor | None, n_buckets: int, n
                                  buckets.data_ptr(), ties.data_ptr(), ws.data_ptr(), nbytes, _stream())
     _check(st, "reformer_lsh_hash")
     return (buckets, ties) if return_near_ties else buckets
+
+
+def lsh_hash_noalloc(qk: torch.Tensor, rotations: torch.Tensor | None, n_buckets: int, n_rounds: int | None = None,
+                     buckets: torch.Tensor | None = None, near_ties: torch.Tensor | None = None):
+    """``reformer_lsh_hash_noalloc``: as ``lsh_hash`` with the library's static
+    device scratch instead of a workspace.  ``buckets`` / ``near_ties`` may be
+    passed in (then this function allocates nothing either)."""
+    B, H, L, d = qk.shape
+    if n_rounds is None:
+        if rotations is None:
+            raise ValueError("n_rounds is needed when rotations is None")
+        n_rounds = rotations.shape[0]
+    rot_ptr = None
+    if n_buckets > 1:
+        if rotations is None or rotations.dtype != torch.float32 or tuple(rotations.shape) != (n_rounds, d, n_buckets // 2):
+            raise ValueError("rotations must be float32 [n_rounds, d, n_buckets/2]")
+        rot_ptr = _dev(rotations, "rotations")
+    if buckets is None:
+        buckets = torch.empty((B, H, n_rounds, L), dtype=torch.int32, device=qk.device)
+    elif buckets.dtype != torch.int32 or tuple(buckets.shape) != (B, H, n_rounds, L):
+        raise ValueError("buckets must be int32 [B, H, n_rounds, L]")
+    ties_ptr = None if near_ties is None else _dev(near_ties, "near_ties")
+    st = lib().reformer_lsh_hash_noalloc(_dev(qk, "qk"), _dtype_code(qk), rot_ptr, B, H, L, d, n_rounds, n_buckets,
+                                         _dev(buckets, "buckets"), ties_ptr, _stream())
+    _check(st, "reformer_lsh_hash_noalloc")
+    return buckets
 
 
 def sort_workspace_bytes(batch, heads, seq_len, n_rounds, n_buckets) -> int:

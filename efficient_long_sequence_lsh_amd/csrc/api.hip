@@ -7,9 +7,16 @@
 
 #include <algorithm>
 #include <limits>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.hpp"
+
+// Scratch of the allocation-free hash entry point: a file-scope device array
+// (every GPU the library runs on holds its own copy until the process ends).
+// Host code never passes this name to a kernel: it is a host-side stand-in.
+// The device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[RLSH_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -160,6 +167,31 @@ hipError_t run_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const i
   return e;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up on the first call per device
+// (with that device current) and kept.
+rlsh_status_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RLSH_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch is tracked for", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(RLSH_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +240,38 @@ rlsh_status_t reformer_lsh_hash(const void* qk, rlsh_dtype_t dtype, const float*
   const rlsh::HashShape hs = rlsh::make_hash_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets);
   return hip_status(rlsh::launch_hash(qk, dtype == RLSH_BF16, rotations, hs, buckets, n_near_ties, workspace, stream),
                     "reformer_lsh_hash");
+}
+
+rlsh_status_t reformer_lsh_hash_noalloc(const void* qk, rlsh_dtype_t dtype, const float* rotations, int batch,
+                                        int heads, int seq_len, int d_head, int n_rounds, int n_buckets,
+                                        int32_t* buckets, int32_t* n_near_ties, hipStream_t stream) {
+  rlsh_status_t st = check_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets, -1);
+  if (st != RLSH_OK) return st;
+  if ((st = check_dtype(dtype)) != RLSH_OK) return st;
+  if (qk == nullptr || buckets == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "qk and buckets must be non-null");
+  if ((st = check_aligned(qk, "qk")) != RLSH_OK) return st;
+  if (n_buckets == 1) {
+    const size_t n = tokens(batch, heads, seq_len) * n_rounds;
+    hipError_t e = rlsh::launch_fill_zero_buckets(buckets, n, stream);
+    if (e == hipSuccess && n_near_ties != nullptr) e = rlsh::launch_fill_zero_buckets(n_near_ties, 1, stream);
+    return hip_status(e, "reformer_lsh_hash_noalloc");
+  }
+  if (rotations == nullptr) return fail(RLSH_ERR_INVALID_ARGUMENT, "rotations must be non-null when n_buckets > 1");
+  const size_t need = hash_ws(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+  if (need > static_cast<size_t>(RLSH_NOALLOC_SCRATCH_BYTES))
+    return fail(RLSH_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of hash scratch; the static scratch of reformer_lsh_hash_noalloc holds "
+                "%zu (use reformer_lsh_hash with a workspace)",
+                need, static_cast<size_t>(RLSH_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != RLSH_OK) return st;
+  // Nothing in the scratch has to start at zero: the set-up kernel writes the
+  // rotation fragments, the transposed copy and the bound maxima, every hash
+  // workgroup writes its near-tie count, and the fix-up reads only the entries
+  // counted by this call.
+  const rlsh::HashShape hs = rlsh::make_hash_shape(batch, heads, seq_len, d_head, n_rounds, n_buckets);
+  return hip_status(rlsh::launch_hash(qk, dtype == RLSH_BF16, rotations, hs, buckets, n_near_ties, ws, stream),
+                    "reformer_lsh_hash_noalloc");
 }
 
 size_t reformer_lsh_sort_workspace_bytes(int batch, int heads, int seq_len, int n_rounds, int n_buckets) {

@@ -119,6 +119,27 @@ rlsh_status_t reformer_lsh_hash(const void* qk, rlsh_dtype_t dtype, const float*
                                 int n_buckets, int32_t* buckets, int32_t* n_near_ties,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------- hash, no allocation ----
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and results as reformer_lsh_hash, with the hash scratch in a
+ * static device array of RLSH_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  No workspace argument; the
+ * function calls no hipMalloc/hipFree.  Shapes whose scratch
+ * (reformer_lsh_hash_workspace_bytes) exceeds the array are rejected with
+ * RLSH_ERR_UNSUPPORTED before any launch; 160 MiB holds every shape up to
+ * 2^20 positions x 8 rounds at 8192 buckets, d = 64 (110 MiB).
+ *
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or host threads) race and must be serialised
+ * by the caller.  Nothing in the array needs to start at zero.
+ */
+#define RLSH_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+rlsh_status_t reformer_lsh_hash_noalloc(const void* qk, rlsh_dtype_t dtype, const float* rotations,
+                                        int batch, int heads, int seq_len, int d_head, int n_rounds,
+                                        int n_buckets, int32_t* buckets, int32_t* n_near_ties,
+                                        hipStream_t stream);
+
 /* ---------------------------------------------------------------- sort ----
  * Stable sort of each (batch, head, round) segment by bucket id; ties keep
  * position order (Summary: "sorted by bucket").

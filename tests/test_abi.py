@@ -73,6 +73,16 @@ def test_attention_rejects_bad_arguments(lib, args, code):
     assert lib.reformer_lsh_last_error()
 
 
+def test_noalloc_hash_rejects_bad_arguments_before_any_hip_call(lib):
+    # null buckets
+    assert lib.reformer_lsh_hash_noalloc(FAKE, 1, FAKE, 1, 1, 64, 64, 1, 8, None, None, None) == 1
+    # no rotations with several buckets
+    assert lib.reformer_lsh_hash_noalloc(FAKE, 1, None, 1, 1, 64, 64, 1, 8, FAKE, None, None) == 1
+    # scratch beyond the static array (4 heads of 512K positions, 8 rounds, 8192 buckets): rejected by size
+    assert lib.reformer_lsh_hash_noalloc(FAKE, 1, FAKE, 1, 4, 524288, 64, 8, 8192, FAKE, None, None) == 2
+    assert b"static scratch" in lib.reformer_lsh_last_error()
+
+
 def test_stage_entry_points_reject_bad_arguments(lib):
     # hash: null buckets
     assert lib.reformer_lsh_hash(FAKE, 1, FAKE, 1, 1, 64, 64, 1, 8, None, None, FAKE, 1 << 20, None) == 1
