@@ -59,6 +59,9 @@ def parse():
                     help="read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output of --profile-stage full and of "
                          "--profile-stage copy for --workload, and record calibrated HBM bytes per launch of each "
                          "kernel (with its source digest) in profiles/traffic.json")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="time a large bf16 GEMM (torch.matmul, hipBLASLt) on random and on constant operands: "
+                         "the matrix-core rate the chip sustains under its power limit, beside the dense peak")
     ap.add_argument("--profile-stage", choices=["full", "hash", "sort", "attend", "combine", "copy"],
                     help="profiling mode: run the prerequisite stages once, then only this stage --steps times "
                          "(copy = a plain 256 MiB device copy for counter calibration); prints its timing")
@@ -693,6 +696,38 @@ def ff_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def mfma_ceiling(args):
+    """Sustained bf16 matrix-core rate of the chip, measured with the vendor
+    GEMM (8192 x 8192 x 8192, bf16 in, float32 accumulate) on iid normal
+    operands, on constant operands and on zeros.  The dense peak assumes the
+    full clock; with operands whose bits toggle the chip reaches its power
+    limit and lowers the clock, so the random-operand rate is the practical
+    ceiling for a kernel that keeps the matrix cores busy on real data."""
+    import torch
+
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    res = {}
+    for label in ("random", "constant", "zeros"):
+        if label == "random":
+            a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+            b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16).t().contiguous()
+        elif label == "constant":
+            a = torch.full((n, n), 0.5, device="cuda", dtype=torch.bfloat16)
+            b = torch.full((n, n), 0.25, device="cuda", dtype=torch.bfloat16)
+        else:
+            a = torch.zeros((n, n), device="cuda", dtype=torch.bfloat16)
+            b = torch.zeros((n, n), device="cuda", dtype=torch.bfloat16)
+        c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+        ms = time_calls(lambda: torch.matmul(a, b, out=c), max(args.steps, 10), max(args.warmup, 3))  # noqa: B023
+        tf = 2.0 * n ** 3 / (ms / 1e3) / 1e12
+        res[label] = {"ms": round(ms, 3), "tflops": round(tf, 1), "frac_of_dense_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(args, f"[mfma-ceiling] {label}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        del a, b, c
+    print(json.dumps({"mfma_ceiling": res, "gemm": f"{n}x{n}x{n} bf16 torch.matmul",
+                      "dense_peak_tflops": MFMA_BF16_PEAK_TFLOPS}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -715,6 +750,9 @@ def main():
         return
     if args.ff:
         ff_bench(args)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling(args)
         return
 
     import numpy as np
