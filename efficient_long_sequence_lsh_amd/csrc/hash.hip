@@ -924,24 +924,37 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
 //    64 consecutive floats per feature), 32 loads in flight per column.
 // Best candidate as (value, bucket): the larger value wins, equal values go
 // to the lower bucket; p == 0 counts as +p (the lower bucket).
+//
+// A team of D / 8 lanes takes one queued (position, round); each lane holds 8
+// features of x (one 16- or 32-byte load) and forms its part of every
+// projection it needs from the transposed float32 copy of R, so all of an
+// entry's loads are issued together.  Listed columns are summed across the
+// team; the 16 columns of a group are reduced and scattered at once, so that
+// each lane ends with the whole projections of 16 / team columns.  Full
+// entries take the whole workgroup: thread t scores columns t, t + 256, ...
+// from R's own [feature][column] layout (a wavefront reads 64 consecutive
+// columns of a feature row), 64 features in flight at a time.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
-                                                         const float* __restrict__ rot, HashShape s,
-                                                         int32_t* __restrict__ buckets,
-                                                         const int32_t* __restrict__ counts, int n_regions, int cap,
-                                                         const int32_t* __restrict__ entries_all, int32_t* n_near_ties) {
-  constexpr int kPer = D / 16;
-  constexpr int kGroups = 256 / 16;
+__global__ __launch_bounds__(256, 4) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
+                                                            const float* __restrict__ rot, HashShape s,
+                                                            int32_t* __restrict__ buckets,
+                                                            const int32_t* __restrict__ counts, int n_regions, int cap,
+                                                            const int32_t* __restrict__ entries_all,
+                                                            int32_t* n_near_ties) {
+  constexpr int kPer = 8;                 // features per lane
+  constexpr int kTeam = D / kPer;         // lanes per entry: 8 at d = 64, 16 at d = 128
+  constexpr int kTeams = 256 / kTeam;
   constexpr int kWaves = 256 / 64;
+  constexpr int kGroupCols = 16;
+  constexpr int kColsPerLane = kGroupCols / kTeam;
+  static_assert(kTeam == 8 || kTeam == 16, "team of 8 or 16 lanes");
   __shared__ double xs[D];
   __shared__ double red_v[kWaves];
   __shared__ int red_b[kWaves];
-  const int sub = threadIdx.x & 15;
-  const int group = threadIdx.x >> 4;
-  auto xval = [&](int tok, int k) -> double {
-    if (BF16) return static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[static_cast<size_t>(tok) * D + k]));
-    return static_cast<double>(static_cast<const float*>(qk_raw)[static_cast<size_t>(tok) * D + k]);
-  };
+  __shared__ int full_list[256];
+  __shared__ int n_full;
+  const int sub = threadIdx.x & (kTeam - 1);
+  const int team = threadIdx.x / kTeam;
   auto offer = [&](double& best_v, int& best_b, double p, int c) {
     const double v = p >= 0.0 ? p : -p;
     const int b = p >= 0.0 ? c : c + s.half;
@@ -958,102 +971,172 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(const void* __restrict_
     const int bh = tok / s.seq_len, pos = tok - bh * s.seq_len;
     buckets[(static_cast<size_t>(bh) * s.n_rounds + round) * s.seq_len + pos] = b;
   };
+  // this lane's 8 features of x (rows are 16-byte aligned, slices 16 or 32 bytes)
+  auto load_x = [&](int tok, double (&xv)[kPer]) {
+    const size_t at = static_cast<size_t>(tok) * D + static_cast<size_t>(sub) * kPer;
+    if (BF16) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(qk_raw) + at);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[2 * i] = static_cast<double>(__uint_as_float(w[i] << 16));
+        xv[2 * i + 1] = static_cast<double>(__uint_as_float(w[i] & 0xffff0000u));
+      }
+    } else {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(qk_raw) + at);
+      const f32x4 a = p[0], b = p[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[i] = static_cast<double>(a[i]);
+        xv[4 + i] = static_cast<double>(b[i]);
+      }
+    }
+  };
+  // this lane's part of x . R[:, col]
+  auto part = [&](const float* Rt, int col, const double (&xv)[kPer]) -> double {
+    const f32x4* r = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(col) * D + sub * kPer);
+    const f32x4 a = r[0], b = r[1];
+    double p = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p += xv[q] * static_cast<double>(a[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p += xv[4 + q] * static_cast<double>(b[q]);
+    return p;
+  };
   int seen = 0;
   for (int region = blockIdx.x; region < n_regions; region += gridDim.x) {
-    const int count = counts[region];
-    seen += count;
     const int32_t* entries = entries_all + 3 * static_cast<size_t>(region) * cap;
-    for (int e = group; e < count; e += kGroups) {
-      const int tok = entries[3 * static_cast<size_t>(e)];
-      const int w1 = entries[3 * static_cast<size_t>(e) + 1];
-      const int w2 = entries[3 * static_cast<size_t>(e) + 2];
+    // The first entries are loaded together with the count (a region holds
+    // at least 256 slots, so the loads stay inside it; slots past the count
+    // are never used).
+    const int count = counts[region];
+    int nxt_tok = entries[3 * static_cast<size_t>(team)];
+    int nxt_w1 = entries[3 * static_cast<size_t>(team) + 1];
+    int nxt_w2 = entries[3 * static_cast<size_t>(team) + 2];
+    const int first_kind = (entries[3 * static_cast<size_t>(threadIdx.x) + 1] >> 16) & 3;
+    seen += count;
+    for (int e = team; e < count; e += kTeams) {
+      const int tok = nxt_tok, w1 = nxt_w1, w2 = nxt_w2;
+      if (e + kTeams < count) {
+        nxt_tok = entries[3 * static_cast<size_t>(e + kTeams)];
+        nxt_w1 = entries[3 * static_cast<size_t>(e + kTeams) + 1];
+        nxt_w2 = entries[3 * static_cast<size_t>(e + kTeams) + 2];
+      }
       const int round = w1 & 0xffff;
       const int kind = (w1 >> 16) & 3;
-      if (kind == kTieFull) continue;   // the same for all 16 lanes of the group
+      if (kind == kTieFull) continue;   // the same for all lanes of the team
       const float* Rt = rt + static_cast<size_t>(round) * s.half * D;
       const int a = w2 & 0xffff, b = (w2 >> 16) & 0xffff, c = (w1 >> 18) & 0x1fff;
+      double xv[kPer];
+      load_x(tok, xv);
       double best_v = -1.0;
       int best_b = 0x7fffffff;
-      // listed columns scored cooperatively (features split over the lanes)
-      int cols[3] = {kNoColumn, kNoColumn, kNoColumn};
-      if (kind == kTiePair || kind == kTieTriple) {
-        cols[0] = a;
-        cols[1] = b;
-        if (kind == kTieTriple) cols[2] = c;
-      } else {
-        cols[0] = b;   // the group's extra column, if any
-      }
-      double xv[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) xv[i] = xval(tok, sub * kPer + i);
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        if (cols[j] >= s.half) continue;   // absent or a padding column: the same for the 16 lanes
-        const f32x4* r = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(cols[j]) * D + sub * kPer);
-        double p = 0.0;
-#pragma unroll
-        for (int i = 0; i < kPer / 4; ++i) {
-          const f32x4 v = r[i];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) p += xv[4 * i + q] * static_cast<double>(v[q]);
-        }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) p += shfl_xor_d(p, off);
-        offer(best_v, best_b, p, cols[j]);
-      }
       if (kind == kTieGroup) {
-        // a's group: tile a / 32, lane half (a / 4) % 2; lane i takes its
-        // projection i, column 32 t + 8 (i / 4) + 4 half + i % 4
-        const int col = 32 * (a >> 5) + 8 * (sub >> 2) + 4 * ((a >> 2) & 1) + (sub & 3);
-        if (col < s.half) {
-          const f32x4* rc = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(col) * D);
-          double p = 0.0;
-#pragma unroll 4
-          for (int i = 0; i < D / 4; ++i) {
-            const f32x4 v = rc[i];
+        // a's group: tile a / 32, lane half (a / 4) % 2; its projection j is
+        // column 32 t + 8 (j / 4) + 4 half + j % 4
+        const int base = 32 * (a >> 5) + 4 * ((a >> 2) & 1);
+        auto gcol = [&](int j) { return base + 8 * (j >> 2) + (j & 3); };
+        // in two halves of 8 columns (64 registers of loads in flight each)
+        double pg[kGroupCols];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) p += xval(tok, 4 * i + q) * static_cast<double>(v[q]);
-          }
-          offer(best_v, best_b, p, col);
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int j = 8 * h; j < 8 * h + 8; ++j) pg[j] = gcol(j) < s.half ? part(Rt, gcol(j), xv) : 0.0;
+          asm volatile("" ::: "memory");
         }
-        merge_lanes(best_v, best_b, 8);
+        const double pb = b < s.half ? part(Rt, b, xv) : 0.0;
+        // reduce-scatter over the team: halve the list at each step, keeping
+        // the half this lane's bit selects and adding the partner's copy of it
+#pragma unroll
+        for (int st = 0; (kTeam >> (st + 1)) >= 1; ++st) {
+          const int o = kTeam >> (st + 1);
+          const int n = kGroupCols >> st;
+          const bool up = (sub & o) != 0;
+#pragma unroll
+          for (int i = 0; i < n / 2; ++i) {
+            const double keep = up ? pg[n / 2 + i] : pg[i];
+            const double send = up ? pg[i] : pg[n / 2 + i];
+            pg[i] = keep + shfl_xor_d(send, o);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kColsPerLane; ++i) {
+          const int j = sub * kColsPerLane + i;
+          if (gcol(j) < s.half) offer(best_v, best_b, pg[i], gcol(j));
+        }
+        double sb = pb;
+#pragma unroll
+        for (int off = kTeam / 2; off > 0; off >>= 1) sb += shfl_xor_d(sb, off);
+        if (b < s.half) offer(best_v, best_b, sb, b);
+        merge_lanes(best_v, best_b, kTeam / 2);
+      } else {
+        // pair or triple: the listed columns (absent or padding ones skipped,
+        // the same for the whole team)
+        const int cols[3] = {a, b, kind == kTieTriple ? c : kNoColumn};
+        double p[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) p[j] = cols[j] < s.half ? part(Rt, cols[j], xv) : 0.0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+#pragma unroll
+          for (int off = kTeam / 2; off > 0; off >>= 1) p[j] += shfl_xor_d(p[j], off);
+          if (cols[j] < s.half) offer(best_v, best_b, p[j], cols[j]);
+        }
       }
       if (sub == 0) store(tok, round, best_b);
     }
-    // Full entries, one at a time for the whole workgroup (the entry list and
-    // the loop bounds are the same for every thread).
-    for (int e = 0; e < count; ++e) {
-      const int w1 = entries[3 * static_cast<size_t>(e) + 1];
-      if (((w1 >> 16) & 3) != kTieFull) continue;
-      const int tok = entries[3 * static_cast<size_t>(e)];
-      const int round = w1 & 0xffff;
-      __syncthreads();   // earlier readers of xs, red_v and red_b are done
-      if (threadIdx.x < D) xs[threadIdx.x] = xval(tok, threadIdx.x);
+    // Full entries, one at a time for the whole workgroup.  They are found
+    // 256 entries at a time (one load per thread, not one per entry in
+    // sequence) and listed in LDS; the list and its length are the same for
+    // every thread.
+    for (int first = 0; first < count; first += 256) {
+      __syncthreads();   // earlier readers of the list are done
+      if (threadIdx.x == 0) n_full = 0;
       __syncthreads();
-      const float* R = rot + static_cast<size_t>(round) * D * s.half;
-      double best_v = -1.0;
-      int best_b = 0x7fffffff;
-      for (int c = threadIdx.x; c < s.half; c += 256) {
-        double p = 0.0;
-        for (int k0 = 0; k0 < D; k0 += 32) {
-          float rv[32];
-#pragma unroll
-          for (int k = 0; k < 32; ++k) rv[k] = R[static_cast<size_t>(k0 + k) * s.half + c];
-#pragma unroll
-          for (int k = 0; k < 32; ++k) p += xs[k0 + k] * static_cast<double>(rv[k]);
+      if (first + static_cast<int>(threadIdx.x) < count &&
+          (first == 0 ? first_kind : (entries[3 * static_cast<size_t>(first + threadIdx.x) + 1] >> 16) & 3) == kTieFull)
+        full_list[atomicAdd(&n_full, 1)] = first + threadIdx.x;
+      __syncthreads();
+      const int nf = n_full;
+      for (int f = 0; f < nf; ++f) {
+        const int e = full_list[f];
+        const int w1 = entries[3 * static_cast<size_t>(e) + 1];
+        const int tok = entries[3 * static_cast<size_t>(e)];
+        const int round = w1 & 0xffff;
+        __syncthreads();   // earlier readers of xs, red_v and red_b are done
+        if (threadIdx.x < D) {
+          const size_t at = static_cast<size_t>(tok) * D + threadIdx.x;
+          xs[threadIdx.x] = BF16 ? static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[at]))
+                                 : static_cast<double>(static_cast<const float*>(qk_raw)[at]);
         }
-        offer(best_v, best_b, p, c);
-      }
-      merge_lanes(best_v, best_b, 32);
-      if ((threadIdx.x & 63) == 0) {
-        red_v[threadIdx.x >> 6] = best_v;
-        red_b[threadIdx.x >> 6] = best_b;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        for (int w = 1; w < kWaves; ++w)
-          if (red_v[w] > best_v || (red_v[w] == best_v && red_b[w] < best_b)) { best_v = red_v[w]; best_b = red_b[w]; }
-        store(tok, round, best_b);
+        __syncthreads();
+        const float* R = rot + static_cast<size_t>(round) * D * s.half;
+        double best_v = -1.0;
+        int best_b = 0x7fffffff;
+        for (int c = threadIdx.x; c < s.half; c += 256) {
+          double p = 0.0;
+          // 64 features at a time; consecutive threads read consecutive columns
+#pragma unroll
+          for (int k0 = 0; k0 < D; k0 += 64) {
+            float rv[64];
+#pragma unroll
+            for (int k = 0; k < 64; ++k) rv[k] = R[static_cast<size_t>(k0 + k) * s.half + c];
+#pragma unroll
+            for (int k = 0; k < 64; ++k) p += xs[k0 + k] * static_cast<double>(rv[k]);
+            asm volatile("" ::: "memory");
+          }
+          offer(best_v, best_b, p, c);
+        }
+        merge_lanes(best_v, best_b, 32);
+        if ((threadIdx.x & 63) == 0) {
+          red_v[threadIdx.x >> 6] = best_v;
+          red_b[threadIdx.x >> 6] = best_b;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          for (int w = 1; w < kWaves; ++w)
+            if (red_v[w] > best_v || (red_v[w] == best_v && red_b[w] < best_b)) { best_v = red_v[w]; best_b = red_b[w]; }
+          store(tok, round, best_b);
+        }
       }
     }
   }
