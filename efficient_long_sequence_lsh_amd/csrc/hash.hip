@@ -51,6 +51,7 @@
 #include "internal.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace rlsh {
 
@@ -146,7 +147,7 @@ struct NearTieList {
 enum NearTieKind : int {
   kTiePair = 0,     // columns a, b
   kTieTriple = 1,   // columns a, b, c
-  kTieGroup = 2,    // the 16 columns of a's group (one lane's projections of one tile), plus column b unless 0xffff
+  kTieGroup = 2,    // the 16 x 2^g columns of a's group (one lane's projections of 2^g tiles), plus column b unless 0xffff
   kTieFull = 3,     // every column
 };
 constexpr int kNoColumn = 0xffff;
@@ -168,8 +169,9 @@ __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int roun
 // below the leader.
 //
 // The four keys are the top four of U, the union of every group's top two
-// (GROUPS: a group is one lane's 16 projections of one tile, code >> 4;
-// otherwise every projection is its own group and the keys are exact).  A
+// (a group is code >> GROUP_SHIFT: on the MFMA path one lane's 16
+// projections of each of 2^g consecutive column tiles, shift 4 + g; with
+// shift 0 every projection is its own group and the keys are exact).  A
 // projection outside U has two larger ones in its own group.  With g(k) the
 // group of key k and m1..m4 the truncated magnitudes:
 //   m1 - m2 > tau: the leader wins outright (the overall second is in U);
@@ -190,7 +192,7 @@ __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int roun
 //                                       -> re-decide every column.
 // positive is the sign of the leader's projection, which picks bucket c1 or
 // c1 + b/2; the float64 re-decisions take their own signs.
-template <bool GROUPS>
+template <int GROUP_SHIFT>
 __device__ __forceinline__ void decide_and_store(const Top4& t, bool positive, bool sign_ok, int col1, int col2,
                                                  int col3, float tau_x, int code_bits, int half, int tok,
                                                  int seq_len, int n_rounds, int round, int32_t* buckets,
@@ -209,9 +211,8 @@ __device__ __forceinline__ void decide_and_store(const Top4& t, bool positive, b
   if (!tiny && !near) return;
   int kind = kTieFull, a = col1, b = col2, c = 0;
   if (!tiny) {
-    constexpr int kShift = GROUPS ? 4 : 0;
-    const uint32_t g1 = (t.k1 & code_mask) >> kShift, g2 = (t.k2 & code_mask) >> kShift;
-    const uint32_t g3 = (t.k3 & code_mask) >> kShift;
+    const uint32_t g1 = (t.k1 & code_mask) >> GROUP_SHIFT, g2 = (t.k2 & code_mask) >> GROUP_SHIFT;
+    const uint32_t g3 = (t.k3 & code_mask) >> GROUP_SHIFT;
     const bool far3 = (m1 - m3) > tau, far4 = (m1 - m4) > tau;
     if (g1 != g2) {
       if (far3) {
@@ -576,12 +577,14 @@ __device__ __forceinline__ i32x8 x_to_fp6(const uint16_t* __restrict__ xrow, boo
 constexpr int kSignAtEndTiles = 32;   // column tiles per round from which SIGN_AT_END is used
 
 // Three wavefronts per SIMD at d = 64 fit only without the running maximum's
-// registers; the running-maximum variant takes two (no spills in the loop).
-template <int D, bool SIGN_AT_END>
-__global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) void hash_mfma_kernel(
+// registers and with one-tile groups; the other variants take two (no spills
+// in the loop).
+template <int D, bool SIGN_AT_END, int LG>
+__global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) ? 2 : 3) void hash_mfma_kernel(
     const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ bound_bits,
     HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
   using FT = FragTile<D>;
+  constexpr int kGT = 1 << LG;                       // column tiles per key group
   constexpr int kSteps = FT::kHiSteps;
   constexpr int kLoSteps = FT::kLoSteps;
   constexpr int kTileVec = FT::kVec;                 // 16-byte units per fragment tile
@@ -662,9 +665,12 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) v
 
   const uint32_t code_mask = (1u << s.code_bits) - 1u;
   const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
-  // Running top four of the per-lane, per-tile top twos (a "group" is one
-  // lane's 16 projections of one tile; decide_and_store says what they bound).
+  // Running top four of the per-lane group top twos (a "group" is one lane's
+  // 16 projections of each of kGT consecutive column tiles of a round;
+  // decide_and_store says what they bound).  gk1, gk2: the top two of the
+  // group in progress.
   Top4 tk[kStrips];
+  uint32_t gk1[kStrips], gk2[kStrips];
   int32_t smax[kStrips];
 #pragma unroll
   for (int st = 0; st < kStrips; ++st) { tk[st] = Top4{0u, 0u, 0u, 0u}; smax[st] = INT32_MIN; }
@@ -696,28 +702,46 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) v
         acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, xf[st][ks], acc[st], 0, 0, 0);
     }
   };
-  // Keys of tile n from acc: acc[i] is the projection on column
-  // 32t + 8(i/4) + 4*half_sel + i%4.
   // Keys of the tile at column-tile index t of its round (tile n = round *
-  // n_ctiles + t).
-  auto keys_tile = [&](const f32x16 (&acc)[kStrips], int t) {
-    const uint32_t tile_code = (static_cast<uint32_t>(t) << 5) | (static_cast<uint32_t>(half_sel) << 4);
+  // n_ctiles + t) from acc: acc[i] is the projection on column
+  // 32t + 8(i/4) + 4*half_sel + i%4.  Its code is
+  //   (t / kGT) << (5 + LG) | half_sel << (4 + LG) | (t % kGT) << 4 | i,
+  // where t % kGT (the tile's place in its group, TL) is known at compile
+  // time, so the per-value code is an inline constant of the and-or; the
+  // group's part of the code joins its top two when the group closes.
+  auto keys_tile = [&](const f32x16 (&acc)[kStrips], int t, auto tl_c) {
+    constexpr uint32_t TL = decltype(tl_c)::value;
+    constexpr uint32_t kC = TL << 4;
 #pragma unroll
     for (int st = 0; st < kStrips; ++st) {
-      const uint32_t a1 = make_key(acc[st][0], keep_mask, 0u);
-      const uint32_t a2 = make_key(acc[st][1], keep_mask, 1u);
-      uint32_t t1 = max(a1, a2), t2 = min(a1, a2);
+      uint32_t t1, t2;
+      if (TL == 0) {
+        const uint32_t a1 = make_key(acc[st][0], keep_mask, kC);
+        const uint32_t a2 = make_key(acc[st][1], keep_mask, kC + 1u);
+        t1 = max(a1, a2);
+        t2 = min(a1, a2);
+      } else {
+        t1 = gk1[st];
+        t2 = gk2[st];
+        top2_push2(t1, t2, make_key(acc[st][0], keep_mask, kC), make_key(acc[st][1], keep_mask, kC + 1u));
+      }
 #pragma unroll
       for (int i = 2; i < 16; i += 2)
-        top2_push2(t1, t2, make_key(acc[st][i], keep_mask, static_cast<uint32_t>(i)),
-                   make_key(acc[st][i + 1], keep_mask, static_cast<uint32_t>(i + 1)));
+        top2_push2(t1, t2, make_key(acc[st][i], keep_mask, kC + static_cast<uint32_t>(i)),
+                   make_key(acc[st][i + 1], keep_mask, kC + static_cast<uint32_t>(i + 1)));
       if (!SIGN_AT_END) {
         int32_t sm = smax[st];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) sm = max(max(sm, __float_as_int(acc[st][i])), __float_as_int(acc[st][i + 1]));
         smax[st] = sm;
       }
-      top4_merge2(tk[st], t1 | tile_code, t2 | tile_code);
+      if (TL == kGT - 1) {
+        const uint32_t gcode = (static_cast<uint32_t>(t >> LG) << (5 + LG)) | (static_cast<uint32_t>(half_sel) << (4 + LG));
+        top4_merge2(tk[st], t1 | gcode, t2 | gcode);
+      } else {
+        gk1[st] = t1;
+        gk2[st] = t2;
+      }
     }
   };
   // After the last tile of a round: merge the two lanes that share each
@@ -735,7 +759,8 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) v
       rho2 = round_bound(bound_bits, kBoundLo, s.n_rounds, s.n_ctiles, round);
     }
     auto col_of = [](uint32_t c) {
-      uint32_t i = c & 15u, hs = (c >> 4) & 1u, tt = c >> 5;
+      const uint32_t i = c & 15u, tl = (c >> 4) & (kGT - 1u), hs = (c >> (4 + LG)) & 1u;
+      const uint32_t tt = ((c >> (5 + LG)) << LG) | tl;
       return static_cast<int>(32u * tt + 8u * (i >> 2) + 4u * hs + (i & 3u));
     };
 #pragma unroll
@@ -784,7 +809,7 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) v
         } else {
           positive = sm >= static_cast<int32_t>(tk[st].k1 & ~code_mask);
         }
-        decide_and_store<true>(tk[st], positive, sign_ok, col1, col_of(c2), col_of(c3), tau_x, s.code_bits, s.half,
+        decide_and_store<4 + LG>(tk[st], positive, sign_ok, col1, col_of(c2), col_of(c3), tau_x, s.code_bits, s.half,
                                tok, s.seq_len, s.n_rounds, round, buckets, lst);
       }
       tk[st] = Top4{0u, 0u, 0u, 0u};
@@ -810,10 +835,11 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) v
   // the vector ALU busy at once.
   f32x16 acc_a[kStrips], acc_b[kStrips];
   int tp = 0, rp = 0;   // column tile and round of the tile whose keys the next step extracts
-  auto step = [&](const u32x4* cur, u32x4* next, f32x16 (&acc)[kStrips], const f32x16 (&prev)[kStrips], int n) {
+  auto step = [&](const u32x4* cur, u32x4* next, f32x16 (&acc)[kStrips], const f32x16 (&prev)[kStrips], int n,
+                  auto tl_c) {
     dma_next(next, n);
     mfma_tile(acc, cur);
-    keys_tile(prev, tp);
+    keys_tile(prev, tp, tl_c);
     // every LDS read of the tile's A operands first, so that none waits
     // behind the MFMAs; then one MFMA per five vector instructions
     __builtin_amdgcn_sched_group_barrier(0x100, kSteps + 2 * kLoSteps, 0);
@@ -830,19 +856,36 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END) ? 2 : 3) v
     }
     __syncthreads();   // also makes every wavefront's near-tie pushes visible to the count below
   };
+  // The loop is unrolled by max(2, kGT) so that buffers and the tiles'
+  // places in their groups are fixed per step (kGT divides n_ctiles, so
+  // tile n - 1, whose keys step n extracts, sits at place (n - 1) % kGT).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1 % kGT>;
+  using I2 = std::integral_constant<int, 2 % kGT>;
+  using I3 = std::integral_constant<int, 3 % kGT>;
+  constexpr int kU = kGT < 2 ? 2 : kGT;
   dma_next(lds1, 0);
   mfma_tile(acc_a, lds0);
   __syncthreads();
   int n = 1;
-  for (; n + 1 < n_total; n += 2) {
-    step(lds1, lds0, acc_b, acc_a, n);
-    step(lds0, lds1, acc_a, acc_b, n + 1);
+  for (; n + kU - 1 < n_total; n += kU) {
+    step(lds1, lds0, acc_b, acc_a, n, I0{});
+    step(lds0, lds1, acc_a, acc_b, n + 1, I1{});
+    if (kU == 4) {
+      step(lds1, lds0, acc_b, acc_a, n + 2, I2{});
+      step(lds0, lds1, acc_a, acc_b, n + 3, I3{});
+    }
   }
-  if (n < n_total) {   // n_total even: tile n (odd) is in lds1
-    step(lds1, lds0, acc_b, acc_a, n);
-    keys_tile(acc_b, tp);
+  if (kU == 4) {   // n = n_total - 3: tiles n .. n + 2 and the keys of the last
+    step(lds1, lds0, acc_b, acc_a, n, I0{});
+    step(lds0, lds1, acc_a, acc_b, n + 1, I1{});
+    step(lds1, lds0, acc_b, acc_a, n + 2, I2{});
+    keys_tile(acc_b, tp, I3{});
+  } else if (n < n_total) {   // n_total even: tile n (odd) is in lds1
+    step(lds1, lds0, acc_b, acc_a, n, I0{});
+    keys_tile(acc_b, tp, I1{});
   } else {
-    keys_tile(acc_a, tp);
+    keys_tile(acc_a, tp, I0{});
   }
   round_end(tp, rp);   // (tp, rp) is now the last tile's position
   __syncthreads();
@@ -901,7 +944,7 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
       // reached that magnitude, the two would share a truncated magnitude, so
       // the gap would be zero and the fix-up would decide
       const bool positive = smax >= static_cast<int32_t>(tk.k1 & ~code_mask);
-      decide_and_store<false>(tk, positive, true, c1, c2, c3, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
+      decide_and_store<0>(tk, positive, true, c1, c2, c3, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
                               s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
     }
   }
@@ -913,24 +956,16 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
 // Re-decide queued (token, round) pairs in float64: products of a bf16 or
 // float32 feature and a float32 rotation entry are exact in float64, and a
 // D-term sum rounds by at most about D * 2^-53 of |x| max_j |R_j|.
-//  * pair, triple and group entries take one group of 16 lanes each.  A
-//    listed column's dot product is split over the lanes by features (lane i
-//    holds features [i*D/16, (i+1)*D/16)) and summed across them; a group's
-//    16 columns go one per lane (a whole dot product each).  Columns are read
-//    from the transposed float32 copy of R (one contiguous row per column).
-//  * full entries (rare: four candidates within the bound) take the whole
-//    workgroup: x staged in LDS as float64, thread t scores columns t,
-//    t + 256, ... from R's original [k][column] layout (a wavefront reads
-//    64 consecutive floats per feature), 32 loads in flight per column.
 // Best candidate as (value, bucket): the larger value wins, equal values go
 // to the lower bucket; p == 0 counts as +p (the lower bucket).
 //
 // A team of D / 8 lanes takes one queued (position, round); each lane holds 8
 // features of x (one 16- or 32-byte load) and forms its part of every
 // projection it needs from the transposed float32 copy of R, so all of an
-// entry's loads are issued together.  Listed columns are summed across the
-// team; the 16 columns of a group are reduced and scattered at once, so that
-// each lane ends with the whole projections of 16 / team columns.  Full
+// entry's loads are issued together; listed columns are summed across the
+// team.  Group entries take one wavefront each: lane j forms the whole
+// projection on the group's column j (up to 64 columns: 16 per tile of a
+// group of up to four tiles), all in one round of loads.  Full
 // entries take the whole workgroup: thread t scores columns t, t + 256, ...
 // from R's own [feature][column] layout (a wavefront reads 64 consecutive
 // columns of a feature row), 64 features in flight at a time.
@@ -946,14 +981,17 @@ __global__ __launch_bounds__(256, 4) void hash_fixup_kernel(const void* __restri
   constexpr int kTeams = 256 / kTeam;
   constexpr int kWaves = 256 / 64;
   constexpr int kGroupCols = 16;
-  constexpr int kColsPerLane = kGroupCols / kTeam;
   static_assert(kTeam == 8 || kTeam == 16, "team of 8 or 16 lanes");
   __shared__ double xs[D];
   __shared__ double red_v[kWaves];
   __shared__ int red_b[kWaves];
   __shared__ int full_list[256];
-  __shared__ int n_full;
+  __shared__ int group_list[256];
+  __shared__ int n_full, n_group;
+  __shared__ double xwave[kWaves][D];
   const int sub = threadIdx.x & (kTeam - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int team = threadIdx.x / kTeam;
   auto offer = [&](double& best_v, int& best_b, double p, int c) {
     const double v = p >= 0.0 ? p : -p;
@@ -1023,79 +1061,91 @@ __global__ __launch_bounds__(256, 4) void hash_fixup_kernel(const void* __restri
       }
       const int round = w1 & 0xffff;
       const int kind = (w1 >> 16) & 3;
-      if (kind == kTieFull) continue;   // the same for all lanes of the team
+      if (kind == kTieFull || kind == kTieGroup) continue;   // the same for all lanes of the team
       const float* Rt = rt + static_cast<size_t>(round) * s.half * D;
       const int a = w2 & 0xffff, b = (w2 >> 16) & 0xffff, c = (w1 >> 18) & 0x1fff;
       double xv[kPer];
       load_x(tok, xv);
       double best_v = -1.0;
       int best_b = 0x7fffffff;
-      if (kind == kTieGroup) {
-        // a's group: tile a / 32, lane half (a / 4) % 2; its projection j is
-        // column 32 t + 8 (j / 4) + 4 half + j % 4
-        const int base = 32 * (a >> 5) + 4 * ((a >> 2) & 1);
-        auto gcol = [&](int j) { return base + 8 * (j >> 2) + (j & 3); };
-        // in two halves of 8 columns (64 registers of loads in flight each)
-        double pg[kGroupCols];
+      // pair or triple: the listed columns (absent or padding ones skipped,
+      // the same for the whole team)
+      const int cols[3] = {a, b, kind == kTieTriple ? c : kNoColumn};
+      double p[3];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+      for (int j = 0; j < 3; ++j) p[j] = cols[j] < s.half ? part(Rt, cols[j], xv) : 0.0;
 #pragma unroll
-          for (int j = 8 * h; j < 8 * h + 8; ++j) pg[j] = gcol(j) < s.half ? part(Rt, gcol(j), xv) : 0.0;
-          asm volatile("" ::: "memory");
-        }
-        const double pb = b < s.half ? part(Rt, b, xv) : 0.0;
-        // reduce-scatter over the team: halve the list at each step, keeping
-        // the half this lane's bit selects and adding the partner's copy of it
+      for (int j = 0; j < 3; ++j) {
 #pragma unroll
-        for (int st = 0; (kTeam >> (st + 1)) >= 1; ++st) {
-          const int o = kTeam >> (st + 1);
-          const int n = kGroupCols >> st;
-          const bool up = (sub & o) != 0;
-#pragma unroll
-          for (int i = 0; i < n / 2; ++i) {
-            const double keep = up ? pg[n / 2 + i] : pg[i];
-            const double send = up ? pg[i] : pg[n / 2 + i];
-            pg[i] = keep + shfl_xor_d(send, o);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < kColsPerLane; ++i) {
-          const int j = sub * kColsPerLane + i;
-          if (gcol(j) < s.half) offer(best_v, best_b, pg[i], gcol(j));
-        }
-        double sb = pb;
-#pragma unroll
-        for (int off = kTeam / 2; off > 0; off >>= 1) sb += shfl_xor_d(sb, off);
-        if (b < s.half) offer(best_v, best_b, sb, b);
-        merge_lanes(best_v, best_b, kTeam / 2);
-      } else {
-        // pair or triple: the listed columns (absent or padding ones skipped,
-        // the same for the whole team)
-        const int cols[3] = {a, b, kind == kTieTriple ? c : kNoColumn};
-        double p[3];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) p[j] = cols[j] < s.half ? part(Rt, cols[j], xv) : 0.0;
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-#pragma unroll
-          for (int off = kTeam / 2; off > 0; off >>= 1) p[j] += shfl_xor_d(p[j], off);
-          if (cols[j] < s.half) offer(best_v, best_b, p[j], cols[j]);
-        }
+        for (int off = kTeam / 2; off > 0; off >>= 1) p[j] += shfl_xor_d(p[j], off);
+        if (cols[j] < s.half) offer(best_v, best_b, p[j], cols[j]);
       }
       if (sub == 0) store(tok, round, best_b);
     }
-    // Full entries, one at a time for the whole workgroup.  They are found
-    // 256 entries at a time (one load per thread, not one per entry in
-    // sequence) and listed in LDS; the list and its length are the same for
-    // every thread.
+    // Group and full entries, found 256 entries at a time (one load per
+    // thread, not one per entry in sequence) and listed in LDS; the lists and
+    // their lengths are the same for every thread.
     for (int first = 0; first < count; first += 256) {
-      __syncthreads();   // earlier readers of the list are done
-      if (threadIdx.x == 0) n_full = 0;
+      __syncthreads();   // earlier readers of the lists are done
+      if (threadIdx.x == 0) {
+        n_full = 0;
+        n_group = 0;
+      }
       __syncthreads();
-      if (first + static_cast<int>(threadIdx.x) < count &&
-          (first == 0 ? first_kind : (entries[3 * static_cast<size_t>(first + threadIdx.x) + 1] >> 16) & 3) == kTieFull)
-        full_list[atomicAdd(&n_full, 1)] = first + threadIdx.x;
+      if (first + static_cast<int>(threadIdx.x) < count) {
+        const int kind = first == 0 ? first_kind : (entries[3 * static_cast<size_t>(first + threadIdx.x) + 1] >> 16) & 3;
+        if (kind == kTieFull) full_list[atomicAdd(&n_full, 1)] = first + threadIdx.x;
+        if (kind == kTieGroup) group_list[atomicAdd(&n_group, 1)] = first + threadIdx.x;
+      }
       __syncthreads();
+      // Group entries, one per wavefront: lane j scores projection j % 16 of
+      // the group's tile j / 16 (a whole dot product, x from LDS), the first
+      // lane past the group (or lane 0 after its own column) the extra
+      // column b.
+      for (int f = wave; f < n_group; f += kWaves) {
+        const int e = group_list[f];
+        const int tok = entries[3 * static_cast<size_t>(e)];
+        const int w1 = entries[3 * static_cast<size_t>(e) + 1];
+        const int w2 = entries[3 * static_cast<size_t>(e) + 2];
+        const int round = w1 & 0xffff;
+        const int a = w2 & 0xffff, b = (w2 >> 16) & 0xffff;
+        double* xw = xwave[wave];
+        for (int k = lane; k < D; k += 64) {
+          const size_t at = static_cast<size_t>(tok) * D + k;
+          xw[k] = BF16 ? static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(qk_raw)[at]))
+                       : static_cast<double>(static_cast<const float*>(qk_raw)[at]);
+        }
+        __builtin_amdgcn_wave_barrier();   // a wavefront's LDS accesses complete in order
+        const float* Rt = rt + static_cast<size_t>(round) * s.half * D;
+        constexpr int kChunk = D == 64 ? 16 : 8;   // 16-byte loads in flight per lane
+        auto dot = [&](int col) -> double {
+          const f32x4* r = reinterpret_cast<const f32x4*>(Rt + static_cast<size_t>(col) * D);
+          double p = 0.0;
+#pragma unroll
+          for (int k0 = 0; k0 < D / 4; k0 += kChunk) {
+            f32x4 rv[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) rv[i] = r[k0 + i];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) p += xw[4 * (k0 + i) + q] * static_cast<double>(rv[i][q]);
+            asm volatile("" ::: "memory");
+          }
+          return p;
+        };
+        const int n_cols = kGroupCols << s.group_log2;
+        const int gt0 = ((a >> 5) >> s.group_log2) << s.group_log2;
+        const int col = 32 * (gt0 + (lane >> 4)) + 8 * ((lane & 15) >> 2) + 4 * ((a >> 2) & 1) + (lane & 3);
+        double best_v = -1.0;
+        int best_b = 0x7fffffff;
+        if (lane < n_cols && col < s.half) offer(best_v, best_b, dot(col), col);
+        const int b_lane = n_cols < 64 ? n_cols : 0;
+        if (lane == b_lane && b < s.half) offer(best_v, best_b, dot(b), b);
+        merge_lanes(best_v, best_b, 32);
+        if (lane == 0) store(tok, round, best_b);
+        __builtin_amdgcn_wave_barrier();   // every lane's reads of xw precede the next entry's writes
+      }
       const int nf = n_full;
       for (int f = 0; f < nf; ++f) {
         const int e = full_list[f];
@@ -1168,6 +1218,14 @@ HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds
   s.n_ctiles = (s.half + 31) / 32;
   // MFMA codes: 4 bits value index, 1 bit lane half, then the tile index.
   s.code_bits = std::max(5 + ceil_log2(s.n_ctiles), ceil_log2(std::max(s.half, 2)));
+  // A key group spans four column tiles when a round's tiles split evenly
+  // into fours, else two, else one (the codes keep the same width) -- at
+  // d = 64 with wide rounds, where the key work outweighs the matrix work
+  // (fewer merges into the running top four: 5.47 against 5.75 ms at 8192
+  // buckets); at d = 128 the matrix cores bind and larger groups measured
+  // slower (0.40 against 0.35 ms at 1024 buckets), so groups stay one tile.
+  s.group_log2 = 0;
+  if (d == 64 && s.n_ctiles >= kSignAtEndTiles) s.group_log2 = s.n_ctiles % 4 == 0 ? 2 : s.n_ctiles % 2 == 0 ? 1 : 0;
   return s;
 }
 
@@ -1190,6 +1248,23 @@ hipError_t launch_fill_zero_buckets(int32_t* buckets, size_t n, hipStream_t stre
   if (grid == 0) grid = 1;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, buckets, n);
   return hipGetLastError();
+}
+
+// Groups of several tiles only at d = 64 with wide rounds (make_hash_shape).
+template <int D, bool SIGN_AT_END>
+void launch_mfma(const HashShape& s, dim3 grid, hipStream_t stream, const uint16_t* x, const u32x4* frag,
+                 const uint32_t* bound, int32_t* buckets, NearTieList lst) {
+  if constexpr (D == 64 && SIGN_AT_END) {
+    if (s.group_log2 == 2) {
+      hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 2>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      return;
+    }
+    if (s.group_log2 == 1) {
+      hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 1>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 0>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
 }
 
 hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const HashShape& s, int32_t* buckets,
@@ -1218,16 +1293,16 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
       hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       if (s.n_ctiles >= kSignAtEndTiles)
-        hipLaunchKernelGGL((hash_mfma_kernel<64, true>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+        launch_mfma<64, true>(s, grid, stream, x, frag, bound, buckets, lst);
       else
-        hipLaunchKernelGGL((hash_mfma_kernel<64, false>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+        launch_mfma<64, false>(s, grid, stream, x, frag, bound, buckets, lst);
     } else {
       hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       if (s.n_ctiles >= kSignAtEndTiles)
-        hipLaunchKernelGGL((hash_mfma_kernel<128, true>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+        launch_mfma<128, true>(s, grid, stream, x, frag, bound, buckets, lst);
       else
-        hipLaunchKernelGGL((hash_mfma_kernel<128, false>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+        launch_mfma<128, false>(s, grid, stream, x, frag, bound, buckets, lst);
     }
   } else {
     const float* x = static_cast<const float*>(qk);

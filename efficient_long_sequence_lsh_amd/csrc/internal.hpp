@@ -17,6 +17,7 @@ struct HashShape {
   int half;        // n_buckets / 2
   int n_ctiles;    // ceil(half / 32): column tiles of 32 rotation columns
   int code_bits;   // bits of the candidate code packed into a projection key
+  int group_log2;  // MFMA path: a key group spans 2^group_log2 consecutive column tiles
 };
 
 HashShape make_hash_shape(int batch, int heads, int seq_len, int d, int n_rounds, int n_buckets);

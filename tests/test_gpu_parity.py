@@ -51,6 +51,9 @@ def test_hash_workloads(nat, name):
     (3, 1, 129, 128, 256, 4, "f32"),
     (1, 1, 300, 64, 16, 70, "bf16"),     # more rounds than the kernel keeps bound maxima for in LDS
     (1, 2, 200, 128, 96, 65, "bf16"),
+    (1, 2, 300, 64, 2176, 2, "bf16"),    # 34 column tiles: key groups of two tiles
+    (1, 1, 257, 64, 2132, 3, "bf16"),    # 34 tiles, the last one padded
+    (2, 1, 200, 64, 2304, 2, "bf16"),    # 36 column tiles: key groups of four tiles
 ])
 def test_hash_shapes(nat, B, H, L, d, nb, r, dtype):
     _say(f"[hash-shape] B{B} H{H} L{L} d{d} b{nb} r{r} {dtype}")
@@ -188,11 +191,13 @@ def _in_bin_case(layout, dtype, L=512, seed=3):
     keys are the two losers.  Exact top-two gaps are s times the token's scale
     (at least 2^-13), far above 1e-5: every id must match the oracle.
 
-    layout "groups": the three columns in different column tiles (the winner
+    layout "groups": the three columns in different key groups (the winner
     is the third key); "same_group": the three in one lane's 16 projections of
     one tile (the winner is not even among that group's top two); "mixed": the
     two losers in one group, the winner in another (the top two keys share a
-    group and the third is within the bound).  Half the
+    group and the third is within the bound); "group_tiles": the three in one
+    lane's projections of three different tiles of one four-tile key group
+    (the key groups at this bucket count).  Half the
     tokens have that structure at scales 2^-3..2^3 and either sign, the rest
     are iid normal; other columns project to at most 0.8 times the leader."""
     import torch
@@ -200,7 +205,8 @@ def _in_bin_case(layout, dtype, L=512, seed=3):
     g = np.random.default_rng(seed)
     d, nb = 64, 8192
     half = nb // 2
-    cols = {"groups": (0, 160, 288), "same_group": (96, 97, 98), "mixed": (0, 160, 161)}[layout]
+    cols = {"groups": (0, 160, 288), "same_group": (96, 97, 98), "mixed": (0, 160, 161),
+            "group_tiles": (0, 40, 72)}[layout]
     rot = g.standard_normal((1, d, half)).astype(np.float32)
     rot[0, 0, :] = g.uniform(-0.8, 0.8, half).astype(np.float32)
     rot[0, 1, :] = g.standard_normal(half).astype(np.float32)
@@ -225,7 +231,8 @@ def _in_bin_case(layout, dtype, L=512, seed=3):
 
 
 @pytest.mark.parametrize("layout,dtype", [("groups", "bf16"), ("same_group", "bf16"), ("mixed", "bf16"),
-                                          ("groups", "f32"), ("same_group", "f32"), ("mixed", "f32")])
+                                          ("group_tiles", "bf16"), ("groups", "f32"), ("same_group", "f32"),
+                                          ("mixed", "f32"), ("group_tiles", "f32")])
 def test_hash_third_candidate_in_bin(nat, layout, dtype):
     """Three candidates in one key truncation bin with the winner ranked third
     by key: the kernel must not re-decide between the top two keys only."""
