@@ -194,18 +194,15 @@ __device__ __forceinline__ void push_near_tie(NearTieList lst, int tok, int roun
 // c1 + b/2; the float64 re-decisions take their own signs.
 template <int GROUP_SHIFT>
 __device__ __forceinline__ void decide_and_store(const Top4& t, bool positive, bool sign_ok, int col1, int col2,
-                                                 int col3, float tau_x, int code_bits, int half, int tok,
-                                                 int seq_len, int n_rounds, int round, int32_t* buckets,
-                                                 NearTieList lst) {
+                                                 int col3, float tau_x, int code_bits, int half, int tok, int round,
+                                                 int32_t* slot, NearTieList lst) {
   const uint32_t code_mask = (1u << code_bits) - 1u;
   const float m1 = key_magnitude(t.k1, code_mask);
   const float m2 = key_magnitude(t.k2, code_mask);
   const float m3 = key_magnitude(t.k3, code_mask);
   const float m4 = key_magnitude(t.k4, code_mask);
   const float tau = tau_x + m1 * __uint_as_float((127u + code_bits - 22u) << 23);
-  const int bucket = col1 + (positive ? 0 : half);
-  const int bh = tok / seq_len, pos = tok - bh * seq_len;
-  buckets[(static_cast<size_t>(bh) * n_rounds + round) * seq_len + pos] = bucket;
+  *slot = col1 + (positive ? 0 : half);   // this (position, round)'s bucket id
   const bool tiny = !(m1 > tau) || !sign_ok;
   const bool near = !((m1 - m2) > tau);
   if (!tiny && !near) return;
@@ -627,6 +624,10 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) 
   // |x| and |x - x6| per strip, needed once per round: kept in LDS (read back
   // through a volatile pointer) rather than in registers the loop is short of.
   __shared__ float2 xnorm[kStrips][kHashThreads];
+  // (batch * heads + head, position) of each lane's token: its bucket ids go
+  // to buckets[(bh * n_rounds + round) * seq_len + pos] (one division here,
+  // none per round end).
+  __shared__ int2 tokpos[kStrips][kHashThreads];
 #pragma unroll
   for (int st = 0; st < kStrips; ++st) {
     const int tok = tok_base + 32 * st + (lane & 31);
@@ -656,6 +657,8 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) 
     err += shfl_xor_f(err, 32);
     // float32 sums of at most 256 squares: relative error below 2^-16
     xnorm[st][threadIdx.x] = make_float2(sqrtf(acc) * (1.0f + 1.0f / 65536.0f), sqrtf(err) * (1.0f + 1.0f / 65536.0f));
+    const int bh = tok / s.seq_len;
+    tokpos[st][threadIdx.x] = make_int2(bh, tok - bh * s.seq_len);
   }
 
   const int n_total = s.n_rounds * s.n_ctiles;
@@ -794,8 +797,15 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) 
       const int32_t sm = SIGN_AT_END ? 0 : max(smax[st], static_cast<int32_t>(shfl_xor_u(static_cast<uint32_t>(smax[st]), 32)));
       int tok = tok_base + 32 * st + lane;
       if (lane < 32 && tok < s.n_tokens) {
-        const volatile float* xnv = reinterpret_cast<const volatile float*>(&xnorm[st][threadIdx.x]);
+        // LDS reads at the round end (volatile, so the values are not kept in
+        // registers across the tile loop; through LDS pointers, so they are
+        // ds_reads, not flat loads that would also wait for the tile copy)
+        typedef const volatile __attribute__((address_space(3))) float lds_cvfloat;
+        typedef const volatile __attribute__((address_space(3))) int lds_cvint;
+        lds_cvfloat* xnv = (lds_cvfloat*)(&xnorm[st][threadIdx.x]);
+        lds_cvint* tpv = (lds_cvint*)(&tokpos[st][threadIdx.x]);
         const float2 xn = make_float2(xnv[0], xnv[1]);
+        int32_t* slot = buckets + (static_cast<size_t>(tpv[0]) * s.n_rounds + round) * s.seq_len + tpv[1];
         const float tau_x = split_gap_bound(xn.x, xn.y, cmax, rho1, rho2);
         bool positive = true, sign_ok = true;
         if (SIGN_AT_END) {
@@ -810,7 +820,7 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) 
           positive = sm >= static_cast<int32_t>(tk[st].k1 & ~code_mask);
         }
         decide_and_store<4 + LG>(tk[st], positive, sign_ok, col1, col_of(c2), col_of(c3), tau_x, s.code_bits, s.half,
-                               tok, s.seq_len, s.n_rounds, round, buckets, lst);
+                                 tok, round, slot, lst);
       }
       tk[st] = Top4{0u, 0u, 0u, 0u};
       smax[st] = INT32_MIN;
@@ -905,6 +915,7 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
   lst.lds_count = &ntie;
   const int tok = blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = tok < s.n_tokens;
+  const int tok_bh = tok / s.seq_len, tok_pos = tok - tok_bh * s.seq_len;
   float x[D];
   float sq = 0.0f;
 #pragma unroll
@@ -944,8 +955,9 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
       // reached that magnitude, the two would share a truncated magnitude, so
       // the gap would be zero and the fix-up would decide
       const bool positive = smax >= static_cast<int32_t>(tk.k1 & ~code_mask);
+      int32_t* slot = buckets + (static_cast<size_t>(tok_bh) * s.n_rounds + round) * s.seq_len + tok_pos;
       decide_and_store<0>(tk, positive, true, c1, c2, c3, guard_tiny(kTauRel * xnorm * cmax, xnorm, cmax),
-                              s.code_bits, s.half, tok, s.seq_len, s.n_rounds, round, buckets, lst);
+                          s.code_bits, s.half, tok, round, slot, lst);
     }
   }
   __syncthreads();
