@@ -573,13 +573,23 @@ __device__ __forceinline__ i32x8 x_to_fp6(const uint16_t* __restrict__ xrow, boo
 // gap would be zero and the fix-up would decide).
 constexpr int kSignAtEndTiles = 32;   // column tiles per round from which SIGN_AT_END is used
 
+// Float64 re-decision of a workgroup's queued (position, round) pairs; the
+// workgroup calls it after its tile loop (defined with the re-decision notes
+// below).
+template <int D, bool BF16>
+__device__ __forceinline__ void fixup_region(const void* __restrict__ qk_raw, const float* __restrict__ rt,
+                                             const float* __restrict__ rot, const HashShape& s,
+                                             int32_t* __restrict__ buckets, const int32_t* __restrict__ entries,
+                                             int count);
+
 // Three wavefronts per SIMD at d = 64 fit only without the running maximum's
 // registers and with one-tile groups; the other variants take two (no spills
 // in the loop).
 template <int D, bool SIGN_AT_END, int LG>
 __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) ? 2 : 3) void hash_mfma_kernel(
     const uint16_t* __restrict__ qk, const u32x4* __restrict__ frag, const uint32_t* __restrict__ bound_bits,
-    HashShape s, int32_t* __restrict__ buckets, NearTieList lst) {
+    const float* __restrict__ rt, const float* __restrict__ rot, HashShape s, int32_t* __restrict__ buckets,
+    NearTieList lst, int32_t* n_near_ties) {
   using FT = FragTile<D>;
   constexpr int kGT = 1 << LG;                       // column tiles per key group
   constexpr int kSteps = FT::kHiSteps;
@@ -899,15 +909,22 @@ __global__ __launch_bounds__(kHashThreads, (D == 128 || !SIGN_AT_END || LG > 0) 
   }
   round_end(tp, rp);   // (tp, rp) is now the last tile's position
   __syncthreads();
-  if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
+  const int n_queued = ntie;   // read after the barrier above
+  if (threadIdx.x == 0) {
+    lst.counts[blockIdx.x] = n_queued;
+    if (n_near_ties != nullptr && n_queued > 0) atomicAdd(n_near_ties, n_queued);
+  }
+  fixup_region<D, true>(qk, rt, rot, s, buckets, lst.entries + 3 * static_cast<size_t>(blockIdx.x) * lst.cap, n_queued);
 }
 
 // ------------------------------------------------- FMA hash (float32) ----
 // One thread per token; rotation tiles of 64 columns staged in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__ qk, const float* __restrict__ rot,
-                                                       const uint32_t* __restrict__ cmax_bits, HashShape s,
-                                                       int32_t* __restrict__ buckets, NearTieList lst) {
+                                                       const uint32_t* __restrict__ cmax_bits,
+                                                       const float* __restrict__ rot_t, HashShape s,
+                                                       int32_t* __restrict__ buckets, NearTieList lst,
+                                                       int32_t* n_near_ties) {
   constexpr int kCols = 64;
   __shared__ float rt[D][kCols];
   __shared__ int ntie;
@@ -961,7 +978,12 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) lst.counts[blockIdx.x] = ntie;
+  const int n_queued = ntie;   // read after the barrier above
+  if (threadIdx.x == 0) {
+    lst.counts[blockIdx.x] = n_queued;
+    if (n_near_ties != nullptr && n_queued > 0) atomicAdd(n_near_ties, n_queued);
+  }
+  fixup_region<D, false>(qk, rot_t, rot, s, buckets, lst.entries + 3 * static_cast<size_t>(blockIdx.x) * lst.cap, n_queued);
 }
 
 // ---------------------------------------------------------- fix-up ----
@@ -981,13 +1003,16 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
 // entries take the whole workgroup: thread t scores columns t, t + 256, ...
 // from R's own [feature][column] layout (a wavefront reads 64 consecutive
 // columns of a feature row), 64 features in flight at a time.
+//
+// The workgroup that hashed a region runs this on its own entries after its
+// tile loop (the entries are its own global writes, visible after the
+// barrier that ends the loop), so the latency-bound re-decisions of one
+// workgroup overlap the matrix work of the others on its compute unit.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256, 4) void hash_fixup_kernel(const void* __restrict__ qk_raw, const float* __restrict__ rt,
-                                                            const float* __restrict__ rot, HashShape s,
-                                                            int32_t* __restrict__ buckets,
-                                                            const int32_t* __restrict__ counts, int n_regions, int cap,
-                                                            const int32_t* __restrict__ entries_all,
-                                                            int32_t* n_near_ties) {
+__device__ __forceinline__ void fixup_region(const void* __restrict__ qk_raw, const float* __restrict__ rt,
+                                             const float* __restrict__ rot, const HashShape& s,
+                                             int32_t* __restrict__ buckets, const int32_t* __restrict__ entries,
+                                             int count) {
   constexpr int kPer = 8;                 // features per lane
   constexpr int kTeam = D / kPer;         // lanes per entry: 8 at d = 64, 16 at d = 128
   constexpr int kTeams = 256 / kTeam;
@@ -1052,18 +1077,14 @@ __global__ __launch_bounds__(256, 4) void hash_fixup_kernel(const void* __restri
     for (int q = 0; q < 4; ++q) p += xv[4 + q] * static_cast<double>(b[q]);
     return p;
   };
-  int seen = 0;
-  for (int region = blockIdx.x; region < n_regions; region += gridDim.x) {
-    const int32_t* entries = entries_all + 3 * static_cast<size_t>(region) * cap;
-    // The first entries are loaded together with the count (a region holds
-    // at least 256 slots, so the loads stay inside it; slots past the count
-    // are never used).
-    const int count = counts[region];
+  {
+    // The first entries are loaded at once (a region holds at least 256
+    // slots, so the loads stay inside it; slots past the count are never
+    // used).
     int nxt_tok = entries[3 * static_cast<size_t>(team)];
     int nxt_w1 = entries[3 * static_cast<size_t>(team) + 1];
     int nxt_w2 = entries[3 * static_cast<size_t>(team) + 2];
     const int first_kind = (entries[3 * static_cast<size_t>(threadIdx.x) + 1] >> 16) & 3;
-    seen += count;
     for (int e = team; e < count; e += kTeams) {
       const int tok = nxt_tok, w1 = nxt_w1, w2 = nxt_w2;
       if (e + kTeams < count) {
@@ -1202,7 +1223,6 @@ __global__ __launch_bounds__(256, 4) void hash_fixup_kernel(const void* __restri
       }
     }
   }
-  if (n_near_ties != nullptr && threadIdx.x == 0 && seen > 0) atomicAdd(n_near_ties, seen);
 }
 
 __global__ void fill_zero_kernel(int32_t* p, size_t n) {
@@ -1265,18 +1285,19 @@ hipError_t launch_fill_zero_buckets(int32_t* buckets, size_t n, hipStream_t stre
 // Groups of several tiles only at d = 64 with wide rounds (make_hash_shape).
 template <int D, bool SIGN_AT_END>
 void launch_mfma(const HashShape& s, dim3 grid, hipStream_t stream, const uint16_t* x, const u32x4* frag,
-                 const uint32_t* bound, int32_t* buckets, NearTieList lst) {
+                 const uint32_t* bound, const float* rt, const float* rot, int32_t* buckets, NearTieList lst,
+                 int32_t* ties) {
   if constexpr (D == 64 && SIGN_AT_END) {
     if (s.group_log2 == 2) {
-      hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 2>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 2>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, rt, rot, s, buckets, lst, ties);
       return;
     }
     if (s.group_log2 == 1) {
-      hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 1>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+      hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 1>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, rt, rot, s, buckets, lst, ties);
       return;
     }
   }
-  hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 0>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, s, buckets, lst);
+  hipLaunchKernelGGL((hash_mfma_kernel<D, SIGN_AT_END, 0>), grid, dim3(kHashThreads), 0, stream, x, frag, bound, rt, rot, s, buckets, lst, ties);
 }
 
 hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const HashShape& s, int32_t* buckets,
@@ -1305,42 +1326,31 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
       hipLaunchKernelGGL((hash_prepare_kernel<64, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       if (s.n_ctiles >= kSignAtEndTiles)
-        launch_mfma<64, true>(s, grid, stream, x, frag, bound, buckets, lst);
+        launch_mfma<64, true>(s, grid, stream, x, frag, bound, rt, rotations, buckets, lst, n_near_ties);
       else
-        launch_mfma<64, false>(s, grid, stream, x, frag, bound, buckets, lst);
+        launch_mfma<64, false>(s, grid, stream, x, frag, bound, rt, rotations, buckets, lst, n_near_ties);
     } else {
       hipLaunchKernelGGL((hash_prepare_kernel<128, true>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
       if (s.n_ctiles >= kSignAtEndTiles)
-        launch_mfma<128, true>(s, grid, stream, x, frag, bound, buckets, lst);
+        launch_mfma<128, true>(s, grid, stream, x, frag, bound, rt, rotations, buckets, lst, n_near_ties);
       else
-        launch_mfma<128, false>(s, grid, stream, x, frag, bound, buckets, lst);
+        launch_mfma<128, false>(s, grid, stream, x, frag, bound, rt, rotations, buckets, lst, n_near_ties);
     }
   } else {
     const float* x = static_cast<const float*>(qk);
     if (s.d == 64) {
       hipLaunchKernelGGL((hash_prepare_kernel<64, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
+      hipLaunchKernelGGL(hash_fma_kernel<64>, grid, dim3(256), 0, stream, x, rotations, bound, rt, s, buckets, lst, n_near_ties);
     } else {
       hipLaunchKernelGGL((hash_prepare_kernel<128, false>), pg, dim3(256), 0, stream, rotations, s.half, s.n_rounds, s.n_ctiles, frag, rt, bound, n_near_ties);
       if (marks) (void)hipEventRecord(marks[0], stream);
-      hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, s, buckets, lst);
+      hipLaunchKernelGGL(hash_fma_kernel<128>, grid, dim3(256), 0, stream, x, rotations, bound, rt, s, buckets, lst, n_near_ties);
     }
   }
+  // the re-decisions run inside the hashing kernels (fixup_region)
   if (marks) (void)hipEventRecord(marks[1], stream);
-  const int fix_blocks = std::min(n_regions, 2048);
-  if (s.d == 64) {
-    if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<64, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
-    else
-      hipLaunchKernelGGL((hash_fixup_kernel<64, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL((hash_fixup_kernel<128, true>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
-    else
-      hipLaunchKernelGGL((hash_fixup_kernel<128, false>), dim3(fix_blocks), dim3(256), 0, stream, qk, rt, rotations, s, buckets, counts, n_regions, cap, list, n_near_ties);
-  }
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();
 }
