@@ -233,7 +233,8 @@ rlsh_status_t reformer_lsh_attention(const void* qk, const void* v, const float*
  * events: RLSH_TIMED_EVENTS caller-created events (hipEventCreate), recorded on
  * `stream` in this order:
  *   0 start            1 after the hash set-up kernels (rotation preparation)
- *   2 after the projection/argmax kernel       3 after the near-tie fix-up
+ *   2 after the projection/argmax kernel (which also re-decides its near-ties)
+ *   3 the same point as 2 (kept so the event layout is stable)
  *   4 after the sort   5 after chunk attention 6 after the round combine
  * (with n_buckets == 1 events 1..3 are recorded where the hash would run; for
  * bf16 inputs with 64-slot chunks the last round's attention launch does the
