@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void hash_prepare_kernel(const float* __restri
     const size_t slot = static_cast<size_t>(r) * n_ctiles + t;   // + term * n_rounds * n_ctiles
     const size_t term = static_cast<size_t>(n_rounds) * n_ctiles;
     max32_to(c < half ? norm_bits_up(sum) : 0u, bound_bits + kBoundCmax * term + slot);
-    // the caller's near-tie total starts from zero (the fix-up kernel adds to it)
+    // the caller's near-tie total starts from zero (the hashing kernels add to it)
     if (threadIdx.x == 0 && t == 0 && r == 0 && n_near_ties != nullptr) *n_near_ties = 0;
     if (FRAG) {
       double sr = 0.0, sl = 0.0;
