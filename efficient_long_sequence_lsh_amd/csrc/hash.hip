@@ -30,10 +30,11 @@
 //     sharing a token merge once per round.
 //   * The leading keys give the two leading candidates and their gap.  When the
 //     gap is below twice a bound on the error of one projection (plus the key
-//     truncation), the (position, round) is queued and a fix-up kernel
-//     re-decides it in float64 over the smallest set of columns that the four
-//     keys prove holds the winner: the top two, the top three, one lane's 16
-//     columns of a tile with or without one more, or all columns (keys rank
+//     truncation), the (position, round) is queued and the workgroup that
+//     hashed it re-decides it in float64 after its tile loop, over the
+//     smallest set of columns that the four keys prove holds the winner: the
+//     top two, the top three, one lane's columns of a key group with or
+//     without one more, or all columns (keys rank
 //     candidates that share a truncation bin by code, not by value, so the
 //     set must cover every candidate not bounded below the leader; see
 //     decide_and_store).  By Cauchy-Schwarz, with x6
