@@ -207,10 +207,29 @@ def stage_work(w):
         combine = {"bytes": N * (r * o_row + d * e)}
     return {
         "hash": {"flops": N * r * d * b, "bytes": N * (d * e + 4 * r)},
-        "sort": {"bytes": N * r * 12},   # bucket ids read by histogram and scatter, perm written
+        "sort": {"bytes": N * r * SORT_BYTES[sort_path(w)]},
         "attend": attend,
         "combine": combine,
     }
+
+
+SORT_KERNELS = {"block": "sort_block_kernel",
+                "tiles": "sort_hist_kernel+sort_scan_kernel+sort_scatter_kernel",
+                "two_pass": "sort_hist_kernel+sort_scan_kernel+sort_scatter_kernel+sort_block_kernel"}
+# Bytes per (position, round) each sort path moves by its design: bucket ids
+# read once (block) or twice (tiles: histogram and scatter) and the
+# permutation written; two passes add the 4-byte entries written and read back.
+SORT_BYTES = {"block": 8, "tiles": 12, "two_pass": 20}
+
+
+def sort_path(w):
+    """Which sort the library runs for this shape (the rule of its sort shape)."""
+    kb = max(0, (w.n_buckets - 1).bit_length())
+    if kb <= 8 and w.seq_len <= 12288:
+        return "block"
+    if kb > 6 and (kb > 10 or w.seq_len > 131072):
+        return "two_pass"
+    return "tiles"
 
 
 def kernel_of_stage(w):
@@ -222,7 +241,7 @@ def kernel_of_stage(w):
     hash_k = "hash_mfma_kernel" if w.dtype == "bf16" else "hash_fma_kernel"
     return {
         "hash": (hash_k, "efficient_long_sequence_lsh_amd/csrc/hash.hip"),
-        "sort": ("sort_hist_kernel+sort_scan_kernel+sort_scatter_kernel", "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
+        "sort": (SORT_KERNELS[sort_path(w)], "efficient_long_sequence_lsh_amd/csrc/sort.hip"),
         "attend": (attend, "efficient_long_sequence_lsh_amd/csrc/attend.hip"),
         "combine": (combine, "efficient_long_sequence_lsh_amd/csrc/attend.hip" if compact_rounds(w)
                     else "efficient_long_sequence_lsh_amd/csrc/combine.hip"),

@@ -40,13 +40,21 @@ hipError_t launch_hash(const void* qk, bool bf16, const float* rotations, const 
                        hipEvent_t* marks = nullptr);
 hipError_t launch_fill_zero_buckets(int32_t* buckets, size_t n, hipStream_t stream);
 
+constexpr int kMaxSortKeyBits = 14;   // bucket ids below 2^14
+
 struct SortShape {
-  int n_seg;       // batch * heads * n_rounds
+  int n_seg;         // batch * heads * n_rounds
   int seq_len;
   int n_buckets;
-  int tile;        // positions per sort tile (one wavefront each)
-  int n_tiles;     // ceil(seq_len / tile)
-  int key_bits;    // ceil(log2(n_buckets))
+  int n_tiles;       // ceil(seq_len / 4096): tile workgroups per segment
+  int key_bits;      // ceil(log2(n_buckets))
+  int n_bins;        // bins of the tile passes: n_buckets, or coarse bins of two passes
+  int bin_bits;      // bits of a bin
+  int bin_shift;     // bin = bucket >> bin_shift; two passes: the low bits sorted second
+  int pos_bits;      // two passes: bits of a position in a 32-bit entry
+  bool block;        // one workgroup per segment (short segments, few buckets)
+  bool two_pass;     // coarse tile pass, then one workgroup per (segment, coarse bin)
+  bool wide_entries; // two passes with 64-bit entries (low bits and position do not fit 32)
 };
 SortShape make_sort_shape(int n_seg, int seq_len, int n_buckets);
 size_t sort_scratch_bytes(const SortShape& s);

@@ -142,7 +142,13 @@ rlsh_status_t reformer_lsh_hash_noalloc(const void* qk, rlsh_dtype_t dtype, cons
 
 /* ---------------------------------------------------------------- sort ----
  * Stable sort of each (batch, head, round) segment by bucket id; ties keep
- * position order (Summary: "sorted by bucket").
+ * position order ("Reformer: The Efficient Transformer" research summary,
+ * Summary: positions are ordered by their bucket).
+ *
+ * workspace  device scratch of reformer_lsh_sort_workspace_bytes(...) bytes,
+ *            16-byte aligned, caller-owned; no contents need to be set.  The
+ *            size is 0 (workspace may be NULL) when one workgroup sorts each
+ *            segment (at most 12288 positions and 256 buckets).
  *
  * buckets   int32 [B, H, n_rounds, L], values in [0, n_buckets); a value
  *           outside that range is clamped into it (sorted as 0 or

@@ -112,7 +112,12 @@ def test_workspace_sizes(lib):
     assert lib.reformer_lsh_workspace_bytes(1, 1, 8, 65536, 96, 4, 1024, 64) == 0   # invalid -> 0
     assert lib.reformer_lsh_workspace_bytes(5, 1, 8, 65536, 128, 4, 1024, 64) == 0  # bad dtype -> 0
     assert lib.reformer_lsh_hash_workspace_bytes(1, 1, 1024, 64, 1, 1) == 0       # one bucket: no scratch
-    assert lib.reformer_lsh_sort_workspace_bytes(2, 4, 4096, 2, 64) > 0
+    # one workgroup per segment (<= 12288 positions, <= 256 buckets): no scratch
+    assert lib.reformer_lsh_sort_workspace_bytes(2, 4, 4096, 2, 64) == 0
+    # tiles of 4096: per-tile bin counts and bin totals
+    assert lib.reformer_lsh_sort_workspace_bytes(1, 8, 65536, 4, 1024) >= 32 * 16 * 1024 * 4 + 32 * 1024 * 4
+    # two passes: 4-byte entries per position and round on top of the counts
+    assert lib.reformer_lsh_sort_workspace_bytes(1, 2, 524288, 8, 8192) >= 16 * 524288 * 4
     assert lib.reformer_lsh_attend_workspace_bytes(0, 2, 4, 4096, 64, 2, 64) >= 2 * 4 * 4096 * 2 * 65 * 4
 
 

@@ -295,6 +295,13 @@ def test_hash_one_bucket(nat):
     (1, 1, 1, 5, 2, False),
     (2, 1, 1, 3000, 1, False),           # one bucket: identity
     (8, 8, 8, 1200, 192, True),          # many segments (block count not a multiple of 8)
+    (1, 1, 2, 200000, 1024, True),       # long segments: coarse pass, then four low bits
+    (1, 2, 1, 140001, 64, False),        # six bits on long segments: still one pass
+    (1, 1, 1, 70000, 2, True),           # two buckets
+    (1, 1, 1, (1 << 24) + 4097, 16384, False),   # low bits and position need 64-bit entries
+    (1, 1, 1, 1000000, 8192, False),     # coarse bins above 12288 entries: counted, then ranked in chunks
+    (3, 1, 1, 12289, 256, False),        # one position more than a single workgroup sorts
+    (2, 1, 3, 12288, 16, True),          # one workgroup per segment, four key bits
 ])
 def test_sort(nat, B, H, r, L, nb, skew):
     import torch
@@ -312,6 +319,19 @@ def test_sort(nat, B, H, r, L, nb, skew):
     want_p, want_i = oracle_perm(keys)
     np.testing.assert_array_equal(host(perm), want_p)
     np.testing.assert_array_equal(host(inv), want_i)
+
+
+@pytest.mark.parametrize("L,nb", [(5000, 128), (70000, 1024), (300000, 8192), (40000, 16384)])
+def test_sort_all_keys_equal(nat, L, nb):
+    """Degenerate input: every position in one bucket, so the sort is the identity."""
+    import torch
+
+    _say(f"[sort-equal] L{L} b{nb}")
+    keys = np.full((1, 1, 2, L), nb // 3, np.int32)
+    perm, inv = nat.lsh_sort(torch.from_numpy(keys).cuda(), nb)
+    want = np.broadcast_to(np.arange(L), (1, 1, 2, L))
+    np.testing.assert_array_equal(host(perm), want)
+    np.testing.assert_array_equal(host(inv), want)
 
 
 def test_sort_clamps_out_of_range_keys(nat):
