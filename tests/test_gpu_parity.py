@@ -302,6 +302,9 @@ def test_hash_one_bucket(nat):
     (1, 1, 1, 1000000, 8192, False),     # coarse bins above 12288 entries: counted, then ranked in chunks
     (3, 1, 1, 12289, 256, False),        # one position more than a single workgroup sorts
     (2, 1, 3, 12288, 16, True),          # one workgroup per segment, four key bits
+    (1, 1, 2, 70000, 1000, False),       # tile pass, bucket count not a power of two
+    (1, 1, 2, 150000, 6000, True),       # two passes, 47 coarse bins (the last one partly used)
+    (1, 1, 1, 200000, 1000, False),      # two passes with four low bits, 63 coarse bins
 ])
 def test_sort(nat, B, H, r, L, nb, skew):
     import torch
