@@ -135,22 +135,13 @@ template <int BITS, int G>
 __device__ __forceinline__ void wave_rank(int (&kr)[G], int n_act, int* lc) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t lower = (1ull << lane) - 1ull;
-  // The ballots of group g + 1 run while group g's count is read; the empty
-  // asm (a compiler barrier) keeps the compiler from hoisting every group's
-  // ballots to the top, which would hold them all in registers.
-  uint64_t peers_next = match_key<BITS>(kr[0], lane < n_act);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (g * kWave >= n_act) break;   // uniform over the wavefront
     const bool act = g * kWave + lane < n_act;
     const int key = kr[g];
-    const uint64_t peers = peers_next;
+    const uint64_t peers = match_key<BITS>(key, act);
     const int before = act ? __hip_atomic_load(&lc[key], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
-    if (g + 1 < G) {
-      int next = kr[g + 1];
-      asm volatile("" : "+v"(next)::"memory");
-      peers_next = match_key<BITS>(next, (g + 1) * kWave + lane < n_act);
-    }
     kr[g] = key << 16 | (before + __popcll(peers & lower));
     if (act && (peers & lower) == 0ull)
       __hip_atomic_store(&lc[key], before + __popcll(peers), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -463,7 +454,6 @@ __global__ __launch_bounds__(kBlkThreads) void sort_block_kernel(const void* __r
         perm[seg_base + slot] = p;
         if (inv != nullptr) inv[seg_base + p] = slot;
       }
-      asm volatile("" ::: "memory");   // one group's LDS reads in flight at a time (register pressure)
     }
     __syncthreads();   // the staged slots, or every read of kbase and the counts, are done
     if (resident) {
