@@ -746,8 +746,25 @@ def mfma_ceiling(args):
         res[label] = {"ms": round(ms, 3), "tflops": round(tf, 1), "frac_of_dense_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(args, f"[mfma-ceiling] {label}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
         del a, b, c
+    # The unfused alternative to the hash at this workload's shape: the vendor
+    # GEMM forming every projection x . R (bf16 out), without the argmax.
+    from efficient_long_sequence_lsh_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    N, d, cols = w.batch * w.heads * w.seq_len, w.d_head, w.n_rounds * (w.n_buckets // 2)
+    unfused = None
+    if cols > 0 and N * cols * 2 <= (8 << 30):
+        x = torch.randn((N, d), device="cuda", generator=g).to(torch.bfloat16)
+        rr = torch.randn((d, cols), device="cuda", generator=g).to(torch.bfloat16)
+        p = torch.empty((N, cols), device="cuda", dtype=torch.bfloat16)
+        ms = time_calls(lambda: torch.matmul(x, rr, out=p), max(args.steps, 10), max(args.warmup, 3))
+        tf = 2.0 * N * d * cols / (ms / 1e3) / 1e12
+        unfused = {"shape": f"{N}x{d} . {d}x{cols}", "ms": round(ms, 3), "tflops": round(tf, 1)}
+        log(args, f"[mfma-ceiling] projections of {w.name} as one bf16 GEMM: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        del x, rr, p
     print(json.dumps({"mfma_ceiling": res, "gemm": f"{n}x{n}x{n} bf16 torch.matmul",
-                      "dense_peak_tflops": MFMA_BF16_PEAK_TFLOPS}), flush=True)
+                      "dense_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "unfused_projection_gemm": unfused}),
+          flush=True)
 
 
 def main():
