@@ -29,6 +29,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 MFMA_FP6_PEAK_TFLOPS = 10100.0  # dense fp6 / fp4 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3    # dense float32 MFMA
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # float32 vector FMA (256 CUs x 128 lanes x 2 flops x 2.4 GHz)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -255,7 +257,11 @@ def roofline_for(stage, ms, w):
     work = stage_work(w)[stage]
     kernel, src = kernel_of_stage(w)[stage]
     secs = ms / 1e3
-    if stage == "hash":
+    if stage == "hash" and w.dtype != "bf16":   # float32 inputs: the FMA kernel on the vector ALU
+        ach = work["flops"] / secs / 1e12
+        rf = {"bound": "alu", "achieved": round(ach, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(ach / FP32_VECTOR_PEAK_TFLOPS, 4)}
+    elif stage == "hash":
         ach = work["flops"] / secs / 1e12
         rf = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
               "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -269,6 +275,38 @@ def roofline_for(stage, ms, w):
     rf["kernel"] = kernel
     rf["traffic"] = measured_traffic(kernel, src, w)
     return rf
+
+
+def path_roofline(ms, w):
+    """The whole forward against its floor: each stage's algorithmic work at its
+    own peak (the hash's projections on the dense bf16 MFMA, or the float32
+    vector ALU for float32 inputs; sort, attention and combine at HBM's 8 TB/s
+    for the bytes the algorithm must move), summed, over the measured time."""
+    work = stage_work(w)
+    hash_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+    floor = {"hash": work["hash"]["flops"] / (hash_peak * 1e12) * 1e3}
+    for name in ("sort", "attend", "combine"):
+        floor[name] = work[name]["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3
+    t_roof = sum(floor.values())
+    return {"t_roof_ms": round(t_roof, 4), "frac": round(t_roof / ms, 4),
+            "stage_floor_ms": {k: round(v, 4) for k, v in floor.items()},
+            "basis": "hash flops at the dense bf16 MFMA peak (float32 vector peak for float32 inputs); "
+                     "sort, attention and combine algorithmic bytes at 8 TB/s; set-up kernel excluded"}
+
+
+def occupancy(st, w):
+    """Bucket occupancy of the library's ids for the workload (hashed once more
+    after the timing): largest and mean bucket size over all (batch, head,
+    round) segments, and the mean number of empty buckets per segment."""
+    import numpy as np
+    import torch
+
+    st.hash()
+    torch.cuda.synchronize()
+    ids = st.buckets.cpu().numpy().reshape(-1, w.seq_len)
+    counts = np.stack([np.bincount(row, minlength=w.n_buckets) for row in ids])
+    return {"max_bucket": int(counts.max()), "mean_bucket": round(w.seq_len / w.n_buckets, 2),
+            "empty_buckets_per_round": round(float((counts == 0).sum(axis=1).mean()), 1)}
 
 
 def measured_traffic(kernel, src, w):
@@ -609,8 +647,6 @@ def local_bench(args):
     print(json.dumps(line), flush=True)
 
 
-MFMA_F32_PEAK_TFLOPS = 157.3
-
 
 def backward_bench(args):
     """Backward pass on the workload: perm from the library's hash and sort,
@@ -871,6 +907,8 @@ def main():
         stages[name] = {"ms": round(stage_ms[name], 4), "kernel": r["kernel"], "achieved": r["achieved"],
                         "unit": r["unit"], "frac": r["frac"]}
     stages["hash_setup"] = {"ms": round(stage_ms["hash_setup"], 4)}
+    path = path_roofline(ms, w)
+    occ = occupancy(st, w)
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -896,6 +934,9 @@ def main():
                    "n_buckets": w.n_buckets, "chunk_len": w.chunk_len, "n_rounds": w.n_rounds, "causal": w.causal,
                    "qk": w.qk_kind},
         "roofline": roof,
+        "head_tokens_per_s": round(w.batch * w.heads * w.seq_len / (ms / 1e3), 1),
+        "path_roofline": path,
+        "occupancy": occ,
         "ms_per_step_spread": spread,
         "memory": memory,
         "stages": stages,
