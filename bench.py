@@ -411,14 +411,16 @@ def cpu_baseline(w, inp, heads):
     dt = time.perf_counter() - t0
     frac = len(pairs) / (w.batch * w.heads)       # share of one forward pass the sample covers
     value = w.tokens * frac / dt
+    affinity = len(os.sched_getaffinity(0))
     try:
         import threadpoolctl
 
         info = threadpoolctl.threadpool_info()
         cores = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        cores = len(os.sched_getaffinity(0))
+        cores = affinity
     return {"value": round(value, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "host": {"cpu_count": os.cpu_count(), "affinity": affinity, "blas_threads": int(cores)},
             "sample": f"{len(pairs)} of {w.batch * w.heads} (batch, head) slices, full length {w.seq_len}, "
                       f"all {w.n_rounds} rounds; {dt:.1f} s wall; value = covered share of one forward's "
                       f"{w.tokens} tokens / wall time"}, results
