@@ -756,6 +756,27 @@ def ff_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def gemm_context(ach_tflops):
+    """What the vendor bf16 GEMM sustains on this machine with iid normal operands
+    (8192 x 8192 x 8192, the practical matrix-core ceiling under the power
+    limit), next to the hash's executed matrix work: its bf16 pass at the
+    algorithmic rate plus the fp6 correction pass, which costs a quarter of
+    the bf16 time per flop."""
+    import torch
+
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16).t().contiguous()
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    ms = time_calls(lambda: torch.matmul(a, b, out=c), 50, 50)
+    del a, b, c
+    gemm = 2.0 * n ** 3 / (ms / 1e3) / 1e12
+    executed = ach_tflops * (1.0 + MFMA_BF16_PEAK_TFLOPS / MFMA_FP6_PEAK_TFLOPS)
+    return {"vendor_bf16_gemm_tflops": round(gemm, 1), "gemm": f"{n}x{n}x{n} torch.matmul, iid normal operands",
+            "hash_executed_tflops": round(executed, 1), "hash_executed_vs_gemm": round(executed / gemm, 4)}
+
+
 def mfma_ceiling(args):
     """Sustained bf16 matrix-core rate of the chip, measured with the vendor
     GEMM (8192 x 8192 x 8192, bf16 in, float32 accumulate) on iid normal
@@ -911,6 +932,7 @@ def main():
     stages["hash_setup"] = {"ms": round(stage_ms["hash_setup"], 4)}
     path = path_roofline(ms, w)
     occ = occupancy(st, w)
+    mfma_ctx = gemm_context(stages["hash"]["achieved"]) if w.dtype == "bf16" else None
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -938,6 +960,7 @@ def main():
         "roofline": roof,
         "head_tokens_per_s": round(w.batch * w.heads * w.seq_len / (ms / 1e3), 1),
         "path_roofline": path,
+        "mfma_context": mfma_ctx,
         "occupancy": occ,
         "ms_per_step_spread": spread,
         "memory": memory,
