@@ -650,6 +650,27 @@ def local_bench(args):
 
 
 
+def backward_work(w):
+    """Algorithmic flops and HBM bytes of one backward with the forward's normaliser.
+
+    Flops per head-token and round: the key role S, dP, dV and dK for the 2m
+    queries that see a key (4 * 2 * 2m * d), the query role S, dP and dQ over
+    the window (3 * 2 * 2m * d).  Bytes per head-token: the stats pass reads
+    out and dout and the saved normaliser and writes Z and D; each round
+    gathers the qk, v and dout rows once and reads the perm entry, Z and D;
+    the float32 dqk and dv rows are written in round 0 and read and written in
+    every later round."""
+    N = w.batch * w.heads * w.seq_len
+    win = min(2 * w.chunk_len, w.seq_len)
+    d, r = w.d_head, w.n_rounds
+    e = 2 if w.dtype == "bf16" else 4
+    flops = N * r * (4 + 3) * 2 * win * d
+    stats = 2 * d * e + 4 + 8
+    gather = 3 * d * e + 4 + 8
+    grads = 2 * 4 * d + (r - 1) * 2 * (2 * 4 * d)
+    return flops, N * (stats + r * gather + grads)
+
+
 def backward_bench(args):
     """Backward pass on the workload: perm from the library's hash and sort,
     out from its forward, dout iid normal; times reformer_lsh_attend_backward.
@@ -662,7 +683,8 @@ def backward_bench(args):
     for float32 inputs): the key role S, dP, dV and dK for the 2m queries that
     see a key (4 * 2 * 2m * d), the query role S, dP and dQ over the window
     (3 * 2 * 2m * d); recomputing the normalisers adds S over the window
-    (2 * 2m * d).
+    (2 * 2m * d).  The pass is bound by its bytes (counted below), so the
+    roofline is HBM's, with the matrix-core fraction beside it.
     """
     import numpy as np
     import torch
@@ -693,12 +715,11 @@ def backward_bench(args):
                               args.steps, args.warmup)
     print(f"[bench] backward with the forward's normaliser {ms:.3f} ms; recomputing it {ms_recompute:.3f} ms",
           file=sys.stderr, flush=True)
-    N = w.batch * w.heads * w.seq_len
-    win = min(2 * w.chunk_len, w.seq_len)
-    flops = N * w.n_rounds * (4 + 3) * 2 * win * w.d_head
+    flops, hbm_bytes = backward_work(w)
     ach = flops / (ms / 1e3) / 1e12
     # bf16 inputs run every contraction on the bf16 MFMA, float32 inputs on the float32 MFMA
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    gbs = hbm_bytes / (ms / 1e3) / 1e9
     line = {
         "metric": "LSH-attention backward tokens/sec (grads wrt qk and v)",
         "value": round(w.tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -707,8 +728,11 @@ def backward_bench(args):
         "config": {"workload": f"backward_{w.name}", "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "d_head": w.d_head, "n_buckets": w.n_buckets, "chunk_len": w.chunk_len, "n_rounds": w.n_rounds,
                    "causal": w.causal, "normaliser": "saved by the forward (lse)"},
-        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(ach / peak, 4), "kernel": "bwd_*_kernel (whole pass)", "traffic": None},
+        # the bytes bind: at the MFMA peak the contractions would take a fraction of the time HBM needs
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "bwd_*_kernel (whole pass)", "traffic": None,
+                     "algorithmic_bytes": int(hbm_bytes),
+                     "mfma": {"achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}},
     }
     print(json.dumps(line), flush=True)
 

@@ -42,3 +42,12 @@ def test_float32_hash_priced_at_the_vector_peak():
     rf = bench.roofline_for("hash", 1.0, w)
     assert rf["bound"] == "alu" and rf["peak"] == 157.3
     assert "executed_mfma_frac" not in rf
+
+
+def test_backward_work_text_64k():
+    w = W.WORKLOADS["text_64k"]
+    flops, nbytes = bench.backward_work(w)
+    assert flops == N_TEXT * 4 * 7 * 2 * 128 * 128
+    # stats 524 B; per round 768 B of rows + 12 B of perm, Z, D; float32 gradient rows:
+    # 1 KB written in round 0, 1 KB read and 1 KB written in rounds 1..3
+    assert nbytes == N_TEXT * (524 + 4 * 780 + 1024 + 3 * 2048)
