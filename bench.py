@@ -637,7 +637,8 @@ def local_bench(args):
     ach = bytes_ / (ms / 1e3) / 1e9
     line = {
         "metric": "local attention fwd tokens/sec",
-        "value": round(N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        # tokens as in the main metric (batch x positions); head-tokens beside them
+        "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded iid normal q, k, v)",
         "config": {"workload": f"local_{w.name}", "batch": B, "heads": H, "seq_len": L, "d_head": d, "chunk_len": m,
@@ -645,6 +646,7 @@ def local_bench(args):
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "local_ring_kernel", "traffic": None},
         "flops_per_token": 4 * window * d,
+        "head_tokens_per_s": round(N / (ms / 1e3), 1),
     }
     print(json.dumps(line), flush=True)
 
