@@ -20,8 +20,9 @@
 // rounded to bf16 for the gradient contractions, whose transposed operands come
 // from the gfx950 transposing LDS read; float32 inputs: every contraction on
 // the float32 MFMA 16x16x4 with rows widened in LDS.
-//   z pass      per (round, query chunk): the query's log2-domain normaliser
-//               over its window (chunks c-1 and c), written per position.
+//   z pass      per round, per query chunk (bf16: runs of chunks per
+//               workgroup): the query's log2-domain normaliser over its
+//               window (chunks c-1 and c), written per position.
 //   stats       per position: Z (log2 domain, over rounds) and D.
 //   key pass    per round, per key chunk c: its keys are seen by the queries
 //               of chunks c and c+1; each wavefront owns 16 keys, streams the
@@ -449,16 +450,6 @@ __device__ __forceinline__ void stage_rows16(uint16_t* dst, const uint16_t* __re
   }
 }
 
-// Row fragment of one shared vector as a bf16 MFMA operand: features
-// 32kk + 8g .. +7 of row `row`.
-template <int D>
-__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 32], const uint16_t* __restrict__ src, size_t row,
-                                               int g) {
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    f[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + row * D + 32 * kk + 8 * g));
-}
-
 template <int D>
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* rowp, int kk, int g) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + 32 * kk + 8 * g));
@@ -509,66 +500,114 @@ __device__ __forceinline__ bf16x8 lds_frag_t(const uint16_t* base, int r0, int d
   return __builtin_bit_cast(bf16x8, a);
 }
 
+// z pass (bf16): grid (runs, bh * n_rounds).  A workgroup walks `run`
+// consecutive chunks of one (batch*head, round) segment, keeping the previous
+// chunk's rows in LDS and taking the queries' fragments from the same LDS
+// rows, so every row is gathered once per round (a workgroup per chunk would
+// gather it three times: as a key of its own chunk, of the next chunk, and as
+// a query); the next chunk's rows are loaded into registers while the current
+// one is computed.  Wavefront w owns queries 16w..16w+15 of the chunk; z2 =
+// log2 sum_j 2^(s_ij * scale_log2) over the valid window keys (-inf when
+// there is none).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_z16_kernel(const uint16_t* __restrict__ qk,
-                                                      const int32_t* __restrict__ perm_all, BwdShape s,
-                                                      float* __restrict__ z2_rounds) {
-  __shared__ BwdTile16<D> sh;
-  constexpr int kP = BwdTile16<D>::kPitch;
-  const int c = blockIdx.x, seg = blockIdx.y;
-  const int bh = seg / s.n_rounds;
+struct alignas(16) ZRunLds {
+  static constexpr int kP = D + 16;   // bf16 per row, as BwdTile16
+  uint16_t qk[2][kBT * kP];           // chunk c in slot c & 1
+  int pos[2][kBT];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_zrun16_kernel(const uint16_t* __restrict__ qk,
+                                                         const int32_t* __restrict__ perm_all, BwdShape s, int run,
+                                                         float* __restrict__ z2_rounds) {
+  __shared__ ZRunLds<D> sh;
+  constexpr int kP = ZRunLds<D>::kP;
+  constexpr int kPieces = kBT * (D / 8);
+  constexpr int kPer = kPieces / 256;   // 16-byte pieces per thread and chunk
+  const int seg = blockIdx.y;
   const int L = s.seq_len;
   const int32_t* perm = perm_all + static_cast<size_t>(seg) * L;
-  const size_t row0 = static_cast<size_t>(bh) * L;
+  const size_t row0 = static_cast<size_t>(seg / s.n_rounds) * L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int qslot = c * kBT + 16 * wave + c16;
-  const int qpos = perm[qslot];
-  bf16x8 qf[D / 32];
-  load_row_frags<D>(qf, qk, row0 + qpos, g);
-  float mrun = -INFINITY, lrun = 0.0f;
-  for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
-    const int kc = c - 1 + h;
-    __syncthreads();
-    stage_rows16<D>(sh.a, qk, perm, kc, row0);
-    if (threadIdx.x < kBT) {
-      sh.pos[threadIdx.x] = perm[kc * kBT + threadIdx.x];
-      sh.slot[threadIdx.x] = kc * kBT + threadIdx.x;
+  const int qrow = 16 * wave + c16;
+  const int c0 = blockIdx.x * run;
+  const int c1 = min(c0 + run, s.n_chunks) - 1;
+
+  u32x4 pr[kPer];
+  int ppos = 0;
+  auto load = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      pr[i] = *reinterpret_cast<const u32x4*>(qk + (row0 + perm[c * kBT + u / (D / 8)]) * D + 8 * (u % (D / 8)));
     }
-    __syncthreads();
+    if (threadIdx.x < kBT) ppos = perm[c * kBT + threadIdx.x];
+  };
+  auto store = [&](int c) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const f32x4 acc = dot_tile16<D>(&sh.a[(16 * kt + c16) * kP], qf, g);   // S^T[key 16kt+4g+j][query c16]
-      float tmax = -INFINITY;
-      float v[4];
+    for (int i = 0; i < kPer; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      *reinterpret_cast<u32x4*>(&sh.qk[c & 1][(u / (D / 8)) * kP + 8 * (u % (D / 8))]) = pr[i];
+    }
+    if (threadIdx.x < kBT) sh.pos[c & 1][threadIdx.x] = ppos;
+  };
+  if (c0 > 0) {
+    load(c0 - 1);
+    store(c0 - 1);
+  }
+  load(c0);
+  store(c0);
+  __syncthreads();
+
+  for (int c = c0; c <= c1; ++c) {
+    const bool more = c < c1;
+    if (more) load(c + 1);
+    const int qslot = c * kBT + qrow;
+    const int qpos = sh.pos[c & 1][qrow];
+    bf16x8 qf[D / 32];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 16 * kt + 4 * g + j;
-        bool ok = sh.slot[kr] != qslot;
-        if (s.causal) ok = ok && sh.pos[kr] < qpos;
-        v[j] = ok ? acc[j] * s.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, v[j]);
+    for (int kk = 0; kk < D / 32; ++kk) qf[kk] = lds_frag<D>(&sh.qk[c & 1][qrow * kP], kk, g);
+    float mrun = -INFINITY, lrun = 0.0f;
+    for (int h = (c > 0 ? 0 : 1); h < 2; ++h) {
+      const int kc = c - 1 + h;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x4 acc = dot_tile16<D>(&sh.qk[kc & 1][(16 * kt + c16) * kP], qf, g);   // S^T[key 16kt+4g+j][query c16]
+        float tmax = -INFINITY;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kr = 16 * kt + 4 * g + j;
+          bool ok = kc * kBT + kr != qslot;
+          if (s.causal) ok = ok && sh.pos[kc & 1][kr] < qpos;
+          v[j] = ok ? acc[j] * s.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, v[j]);
+        }
+        const float mnew = fmaxf(mrun, tmax);
+        if (mnew != -INFINITY) {
+          float add = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) add += exp2f(v[j] - mnew);
+          lrun = lrun * exp2f(mrun - mnew) + add;
+          mrun = mnew;
+        }
       }
-      const float mnew = fmaxf(mrun, tmax);
-      if (mnew != -INFINITY) {
-        float add = 0.0f;
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) add += exp2f(v[j] - mnew);
-        lrun = lrun * exp2f(mrun - mnew) + add;
+    for (int off = 16; off < 64; off <<= 1) {
+      const float om = shfl_xor_f(mrun, off), ol = shfl_xor_f(lrun, off);
+      const float mnew = fmaxf(mrun, om);
+      if (mnew != -INFINITY) {
+        lrun = lrun * exp2f(mrun - mnew) + ol * exp2f(om - mnew);
         mrun = mnew;
       }
     }
+    if (g == 0) z2_rounds[static_cast<size_t>(seg) * L + qpos] = (mrun == -INFINITY) ? -INFINITY : mrun + log2f(lrun);
+    __syncthreads();
+    if (more) store(c + 1);   // into chunk c - 1's slot
+    __syncthreads();
   }
-#pragma unroll
-  for (int off = 16; off < 64; off <<= 1) {
-    const float om = shfl_xor_f(mrun, off), ol = shfl_xor_f(lrun, off);
-    const float mnew = fmaxf(mrun, om);
-    if (mnew != -INFINITY) {
-      lrun = lrun * exp2f(mrun - mnew) + ol * exp2f(om - mnew);
-      mrun = mnew;
-    }
-  }
-  if (g == 0) z2_rounds[static_cast<size_t>(seg) * L + qpos] = (mrun == -INFINITY) ? -INFINITY : mrun + log2f(lrun);
 }
 
 // ------------------------------------------------ fused bf16 backward ----
@@ -927,9 +966,12 @@ hipError_t launch_bwd_typed(const void* qk, const void* v, const void* out, cons
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const uint16_t* o16 = static_cast<const uint16_t*>(dout);
   if (lse == nullptr) {   // per-round normalisers, recomputed
-    if constexpr (BF16)
-      hipLaunchKernelGGL(bwd_z16_kernel<D>, dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, q16, perm, s,
-                         z2_rounds);
+    if constexpr (BF16) {
+      // runs of 4 to 16 chunks measured alike; 32 and 64 slower
+      const int zrun = std::min(8, s.n_chunks);
+      hipLaunchKernelGGL(bwd_zrun16_kernel<D>, dim3((s.n_chunks + zrun - 1) / zrun, bh * s.n_rounds), dim3(256), 0,
+                         stream, q16, perm, s, zrun, z2_rounds);
+    }
     else
       hipLaunchKernelGGL((bwd_z_kernel<D, false>), dim3(s.n_chunks, bh * s.n_rounds), dim3(256), 0, stream, qk, perm,
                          s, z2_rounds);
