@@ -1,6 +1,5 @@
 """The C ABI loads, exports every declared symbol, and rejects bad arguments on
 the host before any HIP call (no GPU needed)."""
-import ctypes
 import os
 import re
 
