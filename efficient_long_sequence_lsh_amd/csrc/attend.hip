@@ -42,7 +42,7 @@ namespace {
 
 constexpr int kQTile = 64;       // sorted slots per query tile (4 waves x 16)
 constexpr int kKTile = 64;       // sorted slots per key tile
-constexpr int kRunTiles = 4;     // query tiles per workgroup
+constexpr int kRunTiles = 4;     // query tiles per workgroup on grids that fill the chip
 
 struct AttnShape {
   int seq_len;
@@ -78,7 +78,8 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void chunk_attend_kernel(const void* __restrict__ qk_raw,
                                                            const void* __restrict__ v_raw,
                                                            const int32_t* __restrict__ perm_all, AttnShape s,
-                                                           float* __restrict__ o_rounds, float* __restrict__ z_rounds) {
+                                                           int run_tiles, float* __restrict__ o_rounds,
+                                                           float* __restrict__ z_rounds) {
   using Lds = AttnLds<D, BF16>;
   __shared__ Lds sh;
 
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(const void* __restric
   const int q16 = lane & 15;      // query column owned by this lane
   const int g = lane >> 4;        // 4-lane group index
 
-  const int qt_begin = blockIdx.x * kRunTiles;
-  const int qt_end = min(s.n_qt, qt_begin + kRunTiles);
+  const int qt_begin = blockIdx.x * run_tiles;
+  const int qt_end = min(s.n_qt, qt_begin + run_tiles);
 
   for (int qt = qt_begin; qt < qt_end; ++qt) {
     const int s0 = qt * kQTile;
@@ -728,8 +729,13 @@ hipError_t launch_fast64(const void* qk, const void* v, const int32_t* perm, int
 template <int D, bool BF16>
 hipError_t launch_typed(const void* qk, const void* v, const int32_t* perm, int n_seg, AttnShape s, float* o, float* z,
                         hipStream_t stream) {
-  dim3 grid((s.n_qt + kRunTiles - 1) / kRunTiles, n_seg);
-  hipLaunchKernelGGL((chunk_attend_kernel<D, BF16>), grid, dim3(256), 0, stream, qk, v, perm, s, o, z);
+  // Each query tile gathers its own key tiles, so a workgroup per tile costs
+  // nothing in reuse: small grids take one tile per workgroup to spread over
+  // more CUs (1024 positions, one head: 16 workgroups instead of 4).
+  const long long grid4 = static_cast<long long>((s.n_qt + kRunTiles - 1) / kRunTiles) * n_seg;
+  const int run = grid4 >= 512 ? kRunTiles : 1;
+  dim3 grid((s.n_qt + run - 1) / run, n_seg);
+  hipLaunchKernelGGL((chunk_attend_kernel<D, BF16>), grid, dim3(256), 0, stream, qk, v, perm, s, run, o, z);
   return hipGetLastError();
 }
 

@@ -927,7 +927,7 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
                                                        int32_t* __restrict__ buckets, NearTieList lst,
                                                        int32_t* n_near_ties) {
   constexpr int kCols = 64;
-  __shared__ float rt[D][kCols];
+  __shared__ __align__(16) float rt[D][kCols];   // 16-byte column quads
   __shared__ int ntie;
   if (threadIdx.x == 0) ntie = 0;
   lst.lds_count = &ntie;
@@ -937,10 +937,14 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
   float x[D];
   float sq = 0.0f;
 #pragma unroll
-  for (int k = 0; k < D; ++k) {
-    x[k] = live ? qk[static_cast<size_t>(tok) * D + k] : 0.0f;
-    sq = fmaf(x[k], x[k], sq);
+  for (int k4 = 0; k4 < D / 4; ++k4) {   // 16-byte loads (rows are 16-byte aligned)
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) v = *reinterpret_cast<const f32x4*>(qk + static_cast<size_t>(tok) * D + 4 * k4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * k4 + e] = v[e];
   }
+#pragma unroll
+  for (int k = 0; k < D; ++k) sq = fmaf(x[k], x[k], sq);
   const float xnorm = sqrtf(sq) * 1.0000005f;
   const uint32_t code_mask = (1u << s.code_bits) - 1u;
   const uint32_t keep_mask = 0x7fffffffu & ~code_mask;
@@ -955,12 +959,22 @@ __global__ __launch_bounds__(256) void hash_fma_kernel(const float* __restrict__
         rt[k][j] = (c0 + j < s.half) ? R[static_cast<size_t>(k) * s.half + c0 + j] : 0.0f;
       }
       __syncthreads();
-      for (int j = 0; j < kCols && c0 + j < s.half; ++j) {
-        float p = 0.0f;
+      // two columns at a time: independent FMA chains (each still summed in k order)
+      const int nj = min(kCols, s.half - c0);
+      for (int j = 0; j < nj; j += 2) {
+        float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-        for (int k = 0; k < D; ++k) p = fmaf(x[k], rt[k][j], p);
-        top4_push(tk, make_key(p, keep_mask, static_cast<uint32_t>(c0 + j)));
-        smax = max(smax, __float_as_int(p));
+        for (int k = 0; k < D; ++k) {
+          const float2 r2 = *reinterpret_cast<const float2*>(&rt[k][j]);
+          p0 = fmaf(x[k], r2.x, p0);
+          p1 = fmaf(x[k], r2.y, p1);
+        }
+        top4_push(tk, make_key(p0, keep_mask, static_cast<uint32_t>(c0 + j)));
+        smax = max(smax, __float_as_int(p0));
+        if (j + 1 < nj) {
+          top4_push(tk, make_key(p1, keep_mask, static_cast<uint32_t>(c0 + j + 1)));
+          smax = max(smax, __float_as_int(p1));
+        }
       }
     }
     const float cmax = round_bound(cmax_bits, kBoundCmax, s.n_rounds, s.n_ctiles, round);
