@@ -277,6 +277,24 @@ def roofline_for(stage, ms, w):
     return rf
 
 
+def other_resource(stage, ms, w):
+    """The stage's rate against the resource that does not bind it: the hash's
+    algorithmic bytes (x read once, ids written) against HBM, and chunk
+    attention's algorithmic matrix work (S = K Q^T and O = V P^T over each
+    chunk's window) against the dense MFMA peak of its operand type."""
+    work = stage_work(w)[stage]
+    secs = ms / 1e3
+    if stage == "hash":
+        ach = work["bytes"] / secs / 1e9
+        return {"hbm": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 4)}}
+    if stage in ("attend", "combine") and "flops" in work:
+        peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        ach = work["flops"] / secs / 1e12
+        return {"mfma": {"achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}}
+    return {}
+
+
 def path_roofline(ms, w):
     """The whole forward against its floor: each stage's algorithmic work at its
     own peak (the hash's projections on the dense bf16 MFMA, or the float32
@@ -954,7 +972,7 @@ def main():
     for name in main:
         r = roofline_for(name, stage_ms[name], w)
         stages[name] = {"ms": round(stage_ms[name], 4), "kernel": r["kernel"], "achieved": r["achieved"],
-                        "unit": r["unit"], "frac": r["frac"]}
+                        "unit": r["unit"], "frac": r["frac"], **other_resource(name, stage_ms[name], w)}
     stages["hash_setup"] = {"ms": round(stage_ms["hash_setup"], 4)}
     path = path_roofline(ms, w)
     occ = occupancy(st, w)

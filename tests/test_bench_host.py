@@ -51,3 +51,22 @@ def test_backward_work_text_64k():
     # stats 524 B; per round 768 B of rows + 12 B of perm, Z, D; float32 gradient rows:
     # 1 KB written in round 0, 1 KB read and 1 KB written in rounds 1..3
     assert nbytes == N_TEXT * (524 + 4 * 780 + 1024 + 3 * 2048)
+
+
+def test_other_resource_text_64k():
+    """The hash against HBM and chunk attention against the bf16 matrix peak:
+    the hash reads each 256-byte qk row once and writes 4 ids of 4 bytes; a
+    chunk of 64 queries against its 128-key window does 2 x 64 x 128 x 128
+    flops for S and as many for O, i.e. 4 x 128 x 128 per query and round."""
+    w = W.WORKLOADS["text_64k"]
+    h = bench.other_resource("hash", 1.0, w)["hbm"]
+    assert math.isclose(h["achieved"], round(N_TEXT * (256 + 16) / 1e-3 / 1e9, 1))
+    assert h["peak"] == 8000.0
+    a = bench.other_resource("attend", 1.0, w)["mfma"]
+    assert math.isclose(a["achieved"], round(N_TEXT * 3 * 4 * 128 * 128 / 1e-3 / 1e12, 2))
+    c = bench.other_resource("combine", 1.0, w)["mfma"]
+    assert math.isclose(c["achieved"], round(N_TEXT * 4 * 128 * 128 / 1e-3 / 1e12, 2))
+    assert a["peak"] == c["peak"] == 2500.0
+    assert bench.other_resource("sort", 1.0, w) == {}
+    # float32 inputs: attention runs on float32 matrix cores
+    assert bench.other_resource("attend", 1.0, W.WORKLOADS["tiny_1k"])["mfma"]["peak"] == 157.3
