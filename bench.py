@@ -195,7 +195,8 @@ def stage_work(w):
     normaliser; the combine reads the r rows and writes the output row.  In the
     compact bf16 pipeline the last round's attention launch does the combine
     itself: "attend" then covers rounds 0..r-2 and "combine" the last round
-    (gather, no o written) plus the reads of the earlier rounds and the output.
+    (gather, no o written) plus the reads of the earlier rounds and the output;
+    its rows are float16 and carry their normaliser in their own bits.
     """
     N = w.batch * w.heads * w.seq_len
     r, d, b = w.n_rounds, w.d_head, w.n_buckets
@@ -203,7 +204,7 @@ def stage_work(w):
     window = min(2 * w.chunk_len, w.seq_len)
     gather = 2 * d * e + 4
     if compact_rounds(w):
-        o_row = 2 * d + 8
+        o_row = 2 * d          # float16 row; z and k ride in its low mantissa bits
         attend = {"bytes": N * (r - 1) * (gather + o_row), "flops": N * (r - 1) * 4 * window * d}
         combine = {"bytes": N * (gather + (r - 1) * o_row + d * e), "flops": N * 4 * window * d}
     else:

@@ -111,7 +111,7 @@ RoundLayout round_layout(rlsh_dtype_t dtype, int batch, int heads, int seq_len, 
   RoundLayout r{};
   r.compact = rlsh::compact_rounds_supported(dtype == RLSH_BF16, seq_len, chunk_len);
   r.o_bytes = a256(n * d_head * (r.compact ? sizeof(uint16_t) : sizeof(float)));
-  r.z_bytes = a256(n * (r.compact ? sizeof(float2) : sizeof(float)));
+  r.z_bytes = r.compact ? 0 : a256(n * sizeof(float));   // compact rows carry their own z
   return r;
 }
 
@@ -152,10 +152,9 @@ hipError_t run_attend(const void* qk, const void* v, rlsh_dtype_t dtype, const i
   const bool bf16 = dtype == RLSH_BF16;
   hipError_t e;
   if (rl.compact) {
-    uint16_t* o16 = static_cast<uint16_t*>(o_mem);
-    float2* zk = static_cast<float2*>(z_mem);
-    e = rlsh::launch_attend_combine_compact(qk, v, perm, bh, seq_len, d_head, n_rounds, causal != 0, o16, zk, out,
-                                            lse, stream, mark);
+    uint16_t* o16 = static_cast<uint16_t*>(o_mem);   // z and k ride in the rows (no z_mem)
+    e = rlsh::launch_attend_combine_compact(qk, v, perm, bh, seq_len, d_head, n_rounds, causal != 0, o16, out, lse,
+                                            stream, mark);
   } else {
     float* o = static_cast<float*>(o_mem);
     float* z = static_cast<float*>(z_mem);

@@ -368,8 +368,12 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& t, Lds64<D>& sh, i
 // Where a round's per-position results go.
 //  kSinkF32:     o float32 [.., d] and z float32 (the stage entry point).
 //  kSinkCompact: o as float16 scaled by 2^-k per row (k = 0 unless the row's
-//                largest magnitude reaches 2^15) and (z, k) as a float pair;
-//                half the bytes of float32 while keeping 11 significant bits.
+//                largest magnitude reaches 2^15), with z and k carried in the
+//                lowest mantissa bit of 48 of the row's values (see
+//                embed_row_meta), so that a round's record at a position is
+//                exactly its row: half the bytes of float32, 10 or 11
+//                significant bits, and no separate 8-byte entry whose sector
+//                the gather at the last round would fetch whole.
 //  kSinkFinal:   the last round of the bf16 pipeline combines in place: it
 //                reads the compact results of the earlier rounds at the
 //                query's position, applies the logsumexp weights (self
@@ -387,11 +391,44 @@ struct RoundSink {
   float* o;              // kSinkF32
   float* z;              // kSinkF32
   uint16_t* o16;         // kSinkCompact: this launch's rounds; kSinkFinal: earlier rounds (read)
-  float2* zk;            // as o16
   const uint16_t* v;     // kSinkFinal: self fallback rows
   uint16_t* out;         // kSinkFinal: output [bh, L, d]
   float* lse;            // kSinkFinal, optional: log of the combined normaliser per position
 };
+
+// A compact row's metadata in its own float16 values.  The row is held by
+// the four lanes q16 + 16g (g = 0..3); lane g has, for dt = 0 .. D/16 - 1, the
+// values of features 16dt + 4g + 0..3 packed two to a dword.  Lanes g = 0, 1
+// and 2 put the low and high halves of z's float bits and k into the lowest
+// mantissa bit of their first 16 values (bit 4dt + j of the piece in value j
+// of step dt); lane 3 keeps its values as rounded.  The bit replaced is at
+// most one unit in the last place of a float16, 2^-10 of the value.
+__device__ __forceinline__ void embed_row_meta(u32x2& pk, int dt, int g, uint32_t piece) {
+  if (dt >= 4) return;
+  const uint32_t keep = g < 3 ? 0xfffefffeu : 0xffffffffu;
+  const uint32_t nib = g < 3 ? (piece >> (4 * dt)) & 15u : 0u;
+  pk[0] = (pk[0] & keep) | (nib & 1u) | ((nib & 2u) << 15);
+  pk[1] = (pk[1] & keep) | ((nib >> 2) & 1u) | ((nib & 8u) << 13);
+}
+
+// The piece a lane carries, from its first four steps' dwords.
+template <int NDT>
+__device__ __forceinline__ uint32_t row_meta_piece(const u32x2 (&h)[NDT]) {
+  uint32_t p = 0u;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    p |= ((h[dt][0] & 1u) | ((h[dt][0] >> 15) & 2u) | ((h[dt][1] & 1u) << 2) | ((h[dt][1] >> 13) & 8u)) << (4 * dt);
+  return p;
+}
+
+// (z, k) of the row whose pieces the four lanes of query row q16 hold; every
+// lane of the wavefront must take part.
+__device__ __forceinline__ float2 row_meta(uint32_t piece, int q16) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16, 64));
+  const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16 + 16, 64));
+  const uint32_t k = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16 + 32, 64));
+  return make_float2(__uint_as_float((lo & 0xffffu) | (hi << 16)), static_cast<float>(k & 0xffu));
+}
 
 // One chunk: queries = rows of buffer `cur`, keys = rows of `prv` (previous
 // chunk, if any) and `cur`.  Writes o and z by original position.
@@ -407,19 +444,17 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
   const int g = lane >> 4;
   const int qrow = 16 * wave + q16;          // query row inside the chunk
   const int qpos = cpos[qrow];
-  // Final-round sink with a compile-time round count: earlier rounds' (z, k)
-  // and this lane's features of their o rows, loaded now.
+  // Final-round sink with a compile-time round count: this lane's features
+  // of the earlier rounds' o rows (which carry their (z, k)), loaded now.
   constexpr bool kPre = MODE > kSinkFinal;
   constexpr int kNP = kPre ? MODE - kSinkFinal - 1 : 0;
   constexpr int kNPA = kNP > 0 ? kNP : 1;
-  float2 zpre[kNPA];
   u32x2 opre[kNPA][D / 16];
   if constexpr (kPre) {
     const size_t prow0 = row0 * (kNP + 1) + qpos;
 #pragma unroll
     for (int rho = 0; rho < kNP; ++rho) {
       const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
-      zpre[rho] = out.zk[pr];
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
         opre[rho][dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
@@ -551,6 +586,8 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
     const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127;
     const int k = e >= 15 ? e - 14 : 0;
     const float down = __uint_as_float(static_cast<uint32_t>(127 - k) << 23) * inv;   // 2^-k / lsum
+    const uint32_t zb = __float_as_uint(zval);
+    const uint32_t piece = g == 0 ? (zb & 0xffffu) : g == 1 ? (zb >> 16) : static_cast<uint32_t>(k);
     uint16_t* op = out.o16 + orow * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -563,24 +600,39 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
       pk[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) |
               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
+      embed_row_meta(pk, dt, g, piece);
       *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = pk;
     }
-    if (g == 0) out.zk[orow] = make_float2(zval, static_cast<float>(k));
   } else {
     // Round combine at this position: rounds 0..n_prev-1 are stored compact
     // at rows (round0 + rho) * L + qpos; this round's o is still in registers.
     const int np = kPre ? kNP : n_prev;
     const size_t prow0 = row0 * (np + 1) + qpos;   // round 0 of this (batch, head)
-    auto zk_of = [&](int rho) -> float2 {
-      if constexpr (kPre) return zpre[rho];
-      return out.zk[prow0 + static_cast<size_t>(rho) * seq_len];
+    // (z, k) of round rho's row: from the prefetched features, or (uncommon
+    // round counts) from the first four steps of the row, read here and again
+    // with the rest of the row when it is added.
+    auto row_meta_of = [&](int rho) -> float2 {
+      u32x2 h[4];
+      if constexpr (kPre) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) h[dt] = opre[rho][dt];
+      } else {
+        const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) h[dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
+      }
+      return row_meta(row_meta_piece(h), q16);
     };
+    float2 zpre[kNPA];
     float zmax = zval;
     if constexpr (kPre) {
 #pragma unroll
-      for (int rho = 0; rho < kNP; ++rho) zmax = fmaxf(zmax, zpre[rho].x);
+      for (int rho = 0; rho < kNP; ++rho) {
+        zpre[rho] = row_meta_of(rho);
+        zmax = fmaxf(zmax, zpre[rho].x);
+      }
     } else {
-      for (int rho = 0; rho < np; ++rho) zmax = fmaxf(zmax, zk_of(rho).x);
+      for (int rho = 0; rho < np; ++rho) zmax = fmaxf(zmax, row_meta_of(rho).x);
     }
     u32x2 res[D / 16];
     float row_lse = -INFINITY;
@@ -618,11 +670,10 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
       } else {
         for (int rho = 0; rho < np; ++rho) {
           const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
-          const float2 e = out.zk[pr];
           u32x2 h[D / 16];
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) h[dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
-          add_round(e, h);
+          add_round(row_meta(row_meta_piece(h), q16), h);
         }
       }
       const float rs = 1.0f / wsum;
@@ -753,7 +804,7 @@ hipError_t launch_chunk_attend(const void* qk, const void* v, bool bf16, const i
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   const int n_seg = bh * n_rounds;
   if (bf16 && s.chunk == kKTile && seq_len % kKTile == 0) {
-    RoundSink out{o_rounds, z_rounds, nullptr, nullptr, nullptr, nullptr, nullptr};
+    RoundSink out{o_rounds, z_rounds, nullptr, nullptr, nullptr, nullptr};
     return d == 64 ? launch_fast64<64, kSinkF32>(qk, v, perm, bh, n_rounds, 0, s, out, stream)
                    : launch_fast64<128, kSinkF32>(qk, v, perm, bh, n_rounds, 0, s, out, stream);
   }
@@ -777,7 +828,7 @@ hipError_t launch_final(const void* qk, const void* v, const int32_t* perm, int 
 }
 
 hipError_t launch_attend_combine_compact(const void* qk, const void* v, const int32_t* perm, int bh, int seq_len,
-                                         int d, int n_rounds, bool causal, uint16_t* o16, float2* zk, void* out,
+                                         int d, int n_rounds, bool causal, uint16_t* o16, void* out,
                                          float* lse, hipStream_t stream, hipEvent_t* mark) {
   AttnShape s{};
   s.seq_len = seq_len;
@@ -786,7 +837,7 @@ hipError_t launch_attend_combine_compact(const void* qk, const void* v, const in
   s.n_qt = seq_len / kKTile;
   s.causal = causal ? 1 : 0;
   s.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-  RoundSink sink{nullptr, nullptr, o16, zk, static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse};
+  RoundSink sink{nullptr, nullptr, o16, static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse};
   hipError_t e = d == 64 ? launch_fast64<64, kSinkCompact>(qk, v, perm, bh, n_rounds - 1, 0, s, sink, stream)
                          : launch_fast64<128, kSinkCompact>(qk, v, perm, bh, n_rounds - 1, 0, s, sink, stream);
   if (e == hipSuccess && mark != nullptr) e = hipEventRecord(*mark, stream);

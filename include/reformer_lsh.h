@@ -196,8 +196,10 @@ rlsh_status_t reformer_lsh_combine(const float* o_rounds, const float* z_rounds,
  * chunk_attend followed by combine, given a permutation.  workspace holds the
  * per-round results: at least reformer_lsh_attend_workspace_bytes().  For
  * bf16 inputs with 64-slot chunks the workspace keeps them compact (o as
- * float16 scaled by a per-row power of two, 11 significant bits); otherwise
- * as float32 (the layout of reformer_lsh_chunk_attend).
+ * float16 scaled by a per-row power of two, with the row's log normaliser and
+ * scale carried in the lowest mantissa bit of 48 of its values: 10 or 11
+ * significant bits); otherwise as float32 (the layout of
+ * reformer_lsh_chunk_attend).
  */
 size_t reformer_lsh_attend_workspace_bytes(rlsh_dtype_t dtype, int batch, int heads, int seq_len,
                                            int d_head, int n_rounds, int chunk_len);
