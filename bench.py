@@ -196,7 +196,8 @@ def stage_work(w):
     compact bf16 pipeline the last round's attention launch does the combine
     itself: "attend" then covers rounds 0..r-2 and "combine" the last round
     (gather, no o written) plus the reads of the earlier rounds and the output;
-    its rows are float16 and carry their normaliser in their own bits.
+    its rows (12-bit block floating point at d = 128, float16 at d = 64) carry
+    their normaliser in their own bits.
     """
     N = w.batch * w.heads * w.seq_len
     r, d, b = w.n_rounds, w.d_head, w.n_buckets
@@ -204,7 +205,9 @@ def stage_work(w):
     window = min(2 * w.chunk_len, w.seq_len)
     gather = 2 * d * e + 4
     if compact_rounds(w):
-        o_row = 2 * d          # float16 row; z and k ride in its low mantissa bits
+        # compact row: 12-bit block floating point at d = 128, float16 at d = 64;
+        # z and the scale exponent ride in the values' lowest bits
+        o_row = 3 * d // 2 if d == 128 else 2 * d
         attend = {"bytes": N * (r - 1) * (gather + o_row), "flops": N * (r - 1) * 4 * window * d}
         combine = {"bytes": N * (gather + (r - 1) * o_row + d * e), "flops": N * 4 * window * d}
     else:

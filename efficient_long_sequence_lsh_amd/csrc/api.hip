@@ -110,7 +110,8 @@ RoundLayout round_layout(rlsh_dtype_t dtype, int batch, int heads, int seq_len, 
   const size_t n = tokens(batch, heads, seq_len) * n_rounds;
   RoundLayout r{};
   r.compact = rlsh::compact_rounds_supported(dtype == RLSH_BF16, seq_len, chunk_len);
-  r.o_bytes = a256(n * d_head * (r.compact ? sizeof(uint16_t) : sizeof(float)));
+  // compact rows: float16 at d = 64, 12-bit block floating point at d = 128
+  r.o_bytes = a256(n * (r.compact ? (d_head == 128 ? 3 * d_head / 2 : 2 * d_head) : d_head * sizeof(float)));
   r.z_bytes = r.compact ? 0 : a256(n * sizeof(float));   // compact rows carry their own z
   return r;
 }

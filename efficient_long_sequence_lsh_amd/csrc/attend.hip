@@ -367,13 +367,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& t, Lds64<D>& sh, i
 
 // Where a round's per-position results go.
 //  kSinkF32:     o float32 [.., d] and z float32 (the stage entry point).
-//  kSinkCompact: o as float16 scaled by 2^-k per row (k = 0 unless the row's
-//                largest magnitude reaches 2^15), with z and k carried in the
-//                lowest mantissa bit of 48 of the row's values (see
-//                embed_row_meta), so that a round's record at a position is
-//                exactly its row: half the bytes of float32, 10 or 11
-//                significant bits, and no separate 8-byte entry whose sector
-//                the gather at the last round would fetch whole.
+//  kSinkCompact: o as a compact row (CompactRow: float16 at d = 64, 12-bit
+//                block floating point at d = 128) that carries its own z and
+//                scale exponent, so a round's record at a position is exactly
+//                its row.
 //  kSinkFinal:   the last round of the bf16 pipeline combines in place: it
 //                reads the compact results of the earlier rounds at the
 //                query's position, applies the logsumexp weights (self
@@ -396,38 +393,136 @@ struct RoundSink {
   float* lse;            // kSinkFinal, optional: log of the combined normaliser per position
 };
 
-// A compact row's metadata in its own float16 values.  The row is held by
-// the four lanes q16 + 16g (g = 0..3); lane g has, for dt = 0 .. D/16 - 1, the
-// values of features 16dt + 4g + 0..3 packed two to a dword.  Lanes g = 0, 1
-// and 2 put the low and high halves of z's float bits and k into the lowest
-// mantissa bit of their first 16 values (bit 4dt + j of the piece in value j
-// of step dt); lane 3 keeps its values as rounded.  The bit replaced is at
-// most one unit in the last place of a float16, 2^-10 of the value.
-__device__ __forceinline__ void embed_row_meta(u32x2& pk, int dt, int g, uint32_t piece) {
-  if (dt >= 4) return;
-  const uint32_t keep = g < 3 ? 0xfffefffeu : 0xffffffffu;
-  const uint32_t nib = g < 3 ? (piece >> (4 * dt)) & 15u : 0u;
-  pk[0] = (pk[0] & keep) | (nib & 1u) | ((nib & 2u) << 15);
-  pk[1] = (pk[1] & keep) | ((nib >> 2) & 1u) | ((nib & 8u) << 13);
+// Compact rows.  A row is held by the four lanes q16 + 16g (g = 0..3); lane g
+// has the D/4 values of features 16dt + 4g + j (dt < D/16, j < 4), value
+// i = 4dt + j of the lane.  Two encodings:
+//   d = 64, float16: value i is the float16 of o * 2^-k (k = 0 unless the
+//     row's largest magnitude reaches 2^15), two to a dword at the feature's
+//     own place in the row (128 bytes);
+//   d = 128, 12-bit block floating point: value i is the integer
+//     q = rne(o * 2^-E) in [-2048, 2047], with E = max(e - 10, -116) for the
+//     row's largest magnitude in [2^e, 2^(e+1)); the lane's 32 integers are
+//     packed at bits 12i of 12 dwords stored at byte 48g of the row (192
+//     bytes, three 64-byte sectors instead of the four of float16).
+//     Absolute error at most 2^(E-1) <= 2^-11 of the row's largest magnitude.
+// Either way lanes g = 0, 1 and 2 carry 16-bit pieces of the row's metadata in
+// the lowest bit of their first 16 values (bit i of the piece in value i):
+// the low and high halves of z's float bits and the scale exponent (k or E)
+// plus 128.  So a round's record at a position is exactly its row, and no
+// separate 8-byte entry has its sector fetched whole by the last round's
+// gather.  The bit replaced costs at most one more unit in the last place
+// (float16: 2^-10 of the value; 12-bit: 2^E) in 48 of the row's values.
+template <int D>
+struct CompactRow {
+  static constexpr bool kBfp = D == 128;
+  static constexpr int kBytes = kBfp ? 3 * D / 2 : 2 * D;   // per row
+  static constexpr int kWords = kBfp ? 12 : D / 8;            // dwords per lane
+};
+
+// The lane's dwords of a stored row.
+template <int D>
+__device__ __forceinline__ void load_row_words(const uint16_t* o16, size_t row, int g,
+                                               uint32_t (&w)[CompactRow<D>::kWords]) {
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(o16) + row * CompactRow<D>::kBytes;
+  if constexpr (CompactRow<D>::kBfp) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(base + 48 * g + 16 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * i + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(base + 2 * (16 * dt + 4 * g));
+      w[2 * dt] = v[0];
+      w[2 * dt + 1] = v[1];
+    }
+  }
 }
 
-// The piece a lane carries, from its first four steps' dwords.
-template <int NDT>
-__device__ __forceinline__ uint32_t row_meta_piece(const u32x2 (&h)[NDT]) {
+// The metadata piece a lane carries (the lowest bits of its first 16 values).
+template <int D>
+__device__ __forceinline__ uint32_t row_meta_piece(const uint32_t (&w)[CompactRow<D>::kWords]) {
   uint32_t p = 0u;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    p |= ((h[dt][0] & 1u) | ((h[dt][0] >> 15) & 2u) | ((h[dt][1] & 1u) << 2) | ((h[dt][1] >> 13) & 8u)) << (4 * dt);
+  for (int i = 0; i < 16; ++i) {
+    const int bit = CompactRow<D>::kBfp ? 12 * i : 16 * i;
+    p |= ((w[bit >> 5] >> (bit & 31)) & 1u) << i;
+  }
   return p;
 }
 
-// (z, k) of the row whose pieces the four lanes of query row q16 hold; every
-// lane of the wavefront must take part.
+// (z, scale exponent) of the row whose pieces the four lanes of query row
+// q16 hold; every lane of the wavefront must take part.
 __device__ __forceinline__ float2 row_meta(uint32_t piece, int q16) {
   const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16, 64));
   const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16 + 16, 64));
-  const uint32_t k = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16 + 32, 64));
-  return make_float2(__uint_as_float((lo & 0xffffu) | (hi << 16)), static_cast<float>(k & 0xffu));
+  const uint32_t ex = static_cast<uint32_t>(__shfl(static_cast<int>(piece), q16 + 32, 64));
+  return make_float2(__uint_as_float((lo & 0xffffu) | (hi << 16)), static_cast<float>(static_cast<int>(ex & 0xffu) - 128));
+}
+
+// Value i of the lane's stored row, without its scale.
+template <int D>
+__device__ __forceinline__ float row_value(const uint32_t (&w)[CompactRow<D>::kWords], int i) {
+  if constexpr (CompactRow<D>::kBfp) {
+    const int bit = 12 * i, k = bit >> 5, off = bit & 31;
+    const uint32_t x = off <= 20 ? w[k] >> off : __builtin_amdgcn_alignbit(w[k + 1], w[k], off);
+    return static_cast<float>(static_cast<int32_t>(x << 20) >> 20);   // sign-extend the low 12 bits
+  } else {
+    const uint32_t x = w[i >> 1];
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>((i & 1) ? x >> 16 : x & 0xffffu)));
+  }
+}
+
+// Encodes this lane's part of a row: o = oacc * inv, z, and writes it.
+// amax is the row's largest |o| (over all four lanes).
+template <int D>
+__device__ __forceinline__ void store_compact_row(uint16_t* o16, size_t row, int g, const f32x4 (&oacc)[D / 16],
+                                                  float inv, float amax, float zval) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+  int ex;
+  float f;
+  if constexpr (CompactRow<D>::kBfp) {
+    ex = max(e - 10, -116);
+    f = __uint_as_float(static_cast<uint32_t>(127 - ex) << 23) * inv;   // 2^-E / lsum
+  } else {
+    ex = e >= 15 ? e - 14 : 0;   // k: the smallest with amax * 2^-k < 2^15
+    f = __uint_as_float(static_cast<uint32_t>(127 - ex) << 23) * inv;
+  }
+  const uint32_t zb = __float_as_uint(zval);
+  const uint32_t piece = g == 0 ? (zb & 0xffffu) : g == 1 ? (zb >> 16) : static_cast<uint32_t>(ex + 128);
+  const uint32_t keep = g < 3 ? ~1u : ~0u;
+  auto meta_bit = [&](int i) -> uint32_t { return (g < 3 && i < 16) ? (piece >> i) & 1u : 0u; };
+  unsigned char* base = reinterpret_cast<unsigned char*>(o16) + row * CompactRow<D>::kBytes;
+  if constexpr (CompactRow<D>::kBfp) {
+    uint32_t w[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) w[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const int q = min(max(static_cast<int>(rintf(oacc[i >> 2][i & 3] * f)), -2048), 2047);
+      uint32_t u = static_cast<uint32_t>(q) & 0xfffu;
+      if (i < 16) u = (u & keep) | meta_bit(i);
+      const int bit = 12 * i, k = bit >> 5, off = bit & 31;
+      w[k] |= u << off;
+      if (off > 20) w[k + 1] |= u >> (32 - off);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      *reinterpret_cast<u32x4*>(base + 48 * g + 16 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      uint32_t h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(oacc[dt][j] * f));
+        if (4 * dt + j < 16) h[j] = (h[j] & keep) | meta_bit(4 * dt + j);
+      }
+      *reinterpret_cast<u32x2*>(base + 2 * (16 * dt + 4 * g)) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    }
+  }
 }
 
 // One chunk: queries = rows of buffer `cur`, keys = rows of `prv` (previous
@@ -449,16 +544,11 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
   constexpr bool kPre = MODE > kSinkFinal;
   constexpr int kNP = kPre ? MODE - kSinkFinal - 1 : 0;
   constexpr int kNPA = kNP > 0 ? kNP : 1;
-  u32x2 opre[kNPA][D / 16];
+  uint32_t opre[kNPA][CompactRow<D>::kWords];
   if constexpr (kPre) {
     const size_t prow0 = row0 * (kNP + 1) + qpos;
 #pragma unroll
-    for (int rho = 0; rho < kNP; ++rho) {
-      const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        opre[rho][dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
-    }
+    for (int rho = 0; rho < kNP; ++rho) load_row_words<D>(out.o16, prow0 + static_cast<size_t>(rho) * seq_len, g, opre[rho]);
   }
   bf16x8 qf[D / 32];
 #pragma unroll
@@ -580,29 +670,7 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
       for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(oacc[dt][j]));
     amax = fmaxf(amax, shfl_xor_f(amax, 16));
     amax = fmaxf(amax, shfl_xor_f(amax, 32));
-    amax *= inv;
-    // k = 0 for rows inside the float16 range, else the smallest k with
-    // amax * 2^-k < 2^15 (exponent arithmetic on the float bits).
-    const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127;
-    const int k = e >= 15 ? e - 14 : 0;
-    const float down = __uint_as_float(static_cast<uint32_t>(127 - k) << 23) * inv;   // 2^-k / lsum
-    const uint32_t zb = __float_as_uint(zval);
-    const uint32_t piece = g == 0 ? (zb & 0xffffu) : g == 1 ? (zb >> 16) : static_cast<uint32_t>(k);
-    uint16_t* op = out.o16 + orow * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      u32x2 pk;
-      const _Float16 h0 = static_cast<_Float16>(oacc[dt][0] * down);
-      const _Float16 h1 = static_cast<_Float16>(oacc[dt][1] * down);
-      const _Float16 h2 = static_cast<_Float16>(oacc[dt][2] * down);
-      const _Float16 h3 = static_cast<_Float16>(oacc[dt][3] * down);
-      pk[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
-              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
-      pk[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) |
-              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
-      embed_row_meta(pk, dt, g, piece);
-      *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = pk;
-    }
+    store_compact_row<D>(out.o16, orow, g, oacc, inv, amax * inv, zval);
   } else {
     // Round combine at this position: rounds 0..n_prev-1 are stored compact
     // at rows (round0 + rho) * L + qpos; this round's o is still in registers.
@@ -612,16 +680,10 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
     // round counts) from the first four steps of the row, read here and again
     // with the rest of the row when it is added.
     auto row_meta_of = [&](int rho) -> float2 {
-      u32x2 h[4];
-      if constexpr (kPre) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) h[dt] = opre[rho][dt];
-      } else {
-        const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) h[dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
-      }
-      return row_meta(row_meta_piece(h), q16);
+      if constexpr (kPre) return row_meta(row_meta_piece<D>(opre[rho]), q16);
+      uint32_t w[CompactRow<D>::kWords];
+      load_row_words<D>(out.o16, prow0 + static_cast<size_t>(rho) * seq_len, g, w);
+      return row_meta(row_meta_piece<D>(w), q16);
     };
     float2 zpre[kNPA];
     float zmax = zval;
@@ -649,31 +711,24 @@ __device__ __forceinline__ void attend_chunk64(const Lds64<D>& sh, int cur, int 
       for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[dt][j] = oacc[dt][j] * c_this;
-      // Adds round rho's stored row (float16 features times 2^k) with its weight.
-      auto add_round = [&](const float2 e, const u32x2 (&h)[D / 16]) {
-        const float w = __expf(e.x - zmax);   // 0 for rounds without a target
-        wsum += w;
-        const float ws = w * __uint_as_float(static_cast<uint32_t>(127 + static_cast<int>(e.y)) << 23);   // w * 2^k
+      // Adds round rho's stored row (values times 2^exponent) with its weight.
+      auto add_round = [&](const float2 e, const uint32_t (&w)[CompactRow<D>::kWords]) {
+        const float wt = __expf(e.x - zmax);   // 0 for rounds without a target
+        wsum += wt;
+        const float ws = wt * __uint_as_float(static_cast<uint32_t>(127 + static_cast<int>(e.y)) << 23);   // wt * 2^ex
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h[dt][q] & 0xffffu));
-            const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h[dt][q] >> 16));
-            acc[dt][2 * q] = fmaf(ws, static_cast<float>(lo), acc[dt][2 * q]);
-            acc[dt][2 * q + 1] = fmaf(ws, static_cast<float>(hi), acc[dt][2 * q + 1]);
-          }
+          for (int j = 0; j < 4; ++j) acc[dt][j] = fmaf(ws, row_value<D>(w, 4 * dt + j), acc[dt][j]);
       };
       if constexpr (kPre) {
 #pragma unroll
         for (int rho = 0; rho < kNP; ++rho) add_round(zpre[rho], opre[rho]);
       } else {
         for (int rho = 0; rho < np; ++rho) {
-          const size_t pr = prow0 + static_cast<size_t>(rho) * seq_len;
-          u32x2 h[D / 16];
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) h[dt] = *reinterpret_cast<const u32x2*>(out.o16 + pr * D + 16 * dt + 4 * g);
-          add_round(row_meta(row_meta_piece(h), q16), h);
+          uint32_t w[CompactRow<D>::kWords];
+          load_row_words<D>(out.o16, prow0 + static_cast<size_t>(rho) * seq_len, g, w);
+          add_round(row_meta(row_meta_piece<D>(w), q16), w);
         }
       }
       const float rs = 1.0f / wsum;

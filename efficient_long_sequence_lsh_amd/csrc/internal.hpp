@@ -71,8 +71,9 @@ hipError_t launch_combine(const float* o_rounds, const float* z_rounds, const vo
                           int bh, int seq_len, int d, int n_rounds, void* out, float* lse, hipStream_t stream);
 
 // Compact per-round intermediates for the bf16 pipeline with 64-slot chunks:
-// o as float16 scaled by 2^-k per row, z and k carried in the lowest
-// mantissa bits of the row's own values.  Rounds
+// o as float16 (d = 64) or 12-bit block floating point (d = 128) rows that
+// carry their own z and scale exponent in the lowest bits of their values
+// (192 bytes per row at d = 128, 2d bytes at d = 64).  Rounds
 // 0..r-2 are stored compact; the last round's launch combines all rounds in
 // place and writes `out` (mark, optional: event recorded between the two).
 bool compact_rounds_supported(bool bf16, int seq_len, int chunk_len);
