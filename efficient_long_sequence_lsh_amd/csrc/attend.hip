@@ -396,9 +396,10 @@ struct RoundSink {
 // Compact rows.  A row is held by the four lanes q16 + 16g (g = 0..3); lane g
 // has the D/4 values of features 16dt + 4g + j (dt < D/16, j < 4), value
 // i = 4dt + j of the lane.  Two encodings:
-//   d = 64, float16: value i is the float16 of o * 2^-k (k = 0 unless the
-//     row's largest magnitude reaches 2^15), two to a dword at the feature's
-//     own place in the row (128 bytes);
+//   d = 64, float16: value i is the float16 of o * 2^-k, k = max(e - 14, -116)
+//     for the row's largest magnitude in [2^e, 2^(e+1)) (so it lands in
+//     [2^14, 2^15) and neither overflows nor falls into subnormals), two to a
+//     dword at the feature's own place in the row (128 bytes);
 //   d = 128, 12-bit block floating point: value i is the integer
 //     q = rne(o * 2^-E) in [-2048, 2047], with E = max(e - 10, -116) for the
 //     row's largest magnitude in [2^e, 2^(e+1)); the lane's 32 integers are
@@ -487,7 +488,7 @@ __device__ __forceinline__ void store_compact_row(uint16_t* o16, size_t row, int
     ex = max(e - 10, -116);
     f = __uint_as_float(static_cast<uint32_t>(127 - ex) << 23) * inv;   // 2^-E / lsum
   } else {
-    ex = e >= 15 ? e - 14 : 0;   // k: the smallest with amax * 2^-k < 2^15
+    ex = max(e - 14, -116);   // k: amax * 2^-k in [2^14, 2^15), tiny rows scaled up
     f = __uint_as_float(static_cast<uint32_t>(127 - ex) << 23) * inv;
   }
   const uint32_t zb = __float_as_uint(zval);

@@ -546,13 +546,17 @@ def test_stage_pipeline_equals_fused_entry(nat):
     np.testing.assert_array_equal(staged, fused)
 
 
-@pytest.mark.parametrize("scale", [1e-3, 1.0, 3e5, 1e30])
-def test_compact_round_storage_keeps_range(nat, scale):
-    """bf16 pipeline stores per-round results compactly (float16 with a per-row
-    power-of-two scale): outputs must track the oracle for tiny and huge values."""
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [1e-30, 1e-3, 1.0, 3e5, 1e30])
+def test_compact_round_storage_keeps_range(nat, scale, d):
+    """bf16 pipeline stores per-round results compactly (float16 at d = 64,
+    12-bit block floating point at d = 128, each with a per-row power-of-two
+    scale and its normaliser in the row's own low bits): outputs must track the
+    oracle for tiny and huge values."""
     import torch
 
-    inp = W.custom_inputs(1, 2, 1024, 64, 32, 2, dtype="bf16", seed=91)
+    _say(f"[compact-range] d{d} scale {scale:g}")
+    inp = W.custom_inputs(1, 2, 1024, d, 32, 2, dtype="bf16", seed=91)
     vb = W.f32_to_bf16_bits((inp.v * scale).astype(np.float32))
     v_exact = W.bf16_bits_to_f32(vb)
     qk, _, rot = to_device(inp)
